@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Throughput of the CSA / HCA hot path on one MI355X.
+
+Default workload: CSA decode at 64K context -- 32 sequences x 16,384
+compressed entries, bf16, 64 query heads x 512, indexer 64 x 128, top-k 1024,
+window 128.  A step is one pass of the path for the whole batch:
+indexer_score -> topk_select -> sparse_mqa_attend (query RMSNorm + RoPE fused
+into the attention prologue, inverse RoPE into its epilogue).
+
+Inputs are resident in HBM before the timed region.  Every decode read set is
+below the 256 MiB Infinity Cache, so the timed steps rotate through several
+copies of the caches at distinct addresses (cold-cache protocol).
+
+Prints ONE JSON line.  ``value`` = query tokens/s (decode) or TFLOP/s
+(prefill).  ``roofline`` rates the dominant kernel against its bound, from HIP
+events on the launch stream; ``cpu_baseline`` times the fp64 oracle on a
+bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP/s"
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+def decode_bytes(sp, N):
+    """Bytes the method must move per query token (one sequence)."""
+    c, d_r = sp.c, sp.d_r
+    row = {"bf16": 2 * c, "fp8mix": (c - d_r) + 2 * d_r, "f32": 4 * c}[sp.kv_format]
+    q = sp.nh * c * 2
+    out = sp.nh * c * 2
+    win = sp.n_win * row
+    if sp.kind == "hca_decode":
+        attend = N * row + win + q + out
+        return dict(attend=attend, total=attend)
+    if sp.index_format == "mxfp4":
+        kI = N * (sp.cI // 2 + sp.cI // 32)
+        qI = sp.nI * (sp.cI // 2 + sp.cI // 32)
+    else:
+        kI = N * sp.cI * 2
+        qI = sp.nI * sp.cI * 2
+    indexer = kI + qI + sp.nI * 4
+    attend = min(sp.k, N) * row + win + q + out
+    return dict(indexer=indexer, attend=attend, total=indexer + attend)
+
+
+def prefill_flops(sp, T):
+    """Algorithmic flops of indexer + attention over a causal prefill."""
+    fi = fa = 0
+    for q in range(T):
+        nv = (q + 1) // sp.m
+        fi += nv * sp.nI * sp.cI * 2
+        fa += (min(sp.k, nv) + min(q + 1, sp.n_win)) * sp.nh * sp.c * 4
+    return fi, fa
+
+
+# ------------------------------------------------------------------ CPU baseline
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline_decode(inp, budget_s=12.0):
+    from oracle import pipeline as OP
+    sp = inp["spec"]
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        OP.decode_reference(inp, n % sp.B)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="query-tokens/s", cores=blas_threads(), kind="oracle",
+                sample=f"{n} query tokens (sequences cycled) of the same workload, fp64 numpy, "
+                       f"{dt:.1f} s")
+
+
+def cpu_baseline_prefill(inp, rows, budget_s=12.0):
+    from oracle import pipeline as OP
+    sp = inp["spec"]
+    t0 = time.perf_counter()
+    caches = OP.prefill_caches(inp)       # compression is not part of the timed path
+    t1 = time.perf_counter()
+    done, flops = 0, 0.0
+    for r in rows:
+        OP.prefill_reference(inp, caches, [r])
+        p = int(inp["q_pos"][r])
+        nv = (p + 1) // sp.m
+        flops += nv * sp.nI * sp.cI * 2 + (min(sp.k, nv) + min(p + 1, sp.n_win)) * sp.nh * sp.c * 4
+        done += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    dt = time.perf_counter() - t1
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+                sample=f"{done} query rows spread over the sequence (indexer+top-k+attention, "
+                       f"fp64 numpy, {dt:.1f} s; compression done beforehand in {t1 - t0:.1f} s)")
+
+
+# ------------------------------------------------------------------ decode bench
+def run_decode(args, torch, I, G):
+    sp = I.CONFIGS[args.config]
+    dev = torch.device("cuda", 0)
+    t0 = time.perf_counter()
+    inp = I.decode_inputs(sp)
+    print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        base = G.upload_decode(inp, dev, stream)
+        copies = [base]
+        for _ in range(args.copies - 1):
+            c = G.Decode(**{k: getattr(base, k) for k in base.__dataclass_fields__})
+            for name in ("kv", "win", "kI", "kI_scale", "qI", "qI_scale", "w", "q", "scores",
+                         "idx", "out"):
+                v = getattr(base, name)
+                if v is not None:
+                    setattr(c, name, v.clone())
+            c.ws = None
+            copies.append(c)
+        for c in copies:                         # workspace sizing outside the timed region
+            G.decode_step(c, stream)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.copies} cache copies resident", file=sys.stderr, flush=True)
+    kinds = ["indexer", "topk", "attend"] if sp.kind == "decode" else ["attend"]
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            G.decode_step(copies[i % len(copies)], stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kinds) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            c = copies[i % len(copies)]
+            e = ev[i]
+            e[0].record(stream)
+            if sp.kind == "decode":
+                G.decode_indexer(c, stream)
+                e[1].record(stream)
+                G.decode_topk(c, stream)
+                e[2].record(stream)
+                G.decode_attend(c, stream=stream)
+                e[3].record(stream)
+            else:
+                G.decode_attend(c, stream=stream)
+                e[1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    per = {k: [] for k in kinds}
+    for e in ev:
+        for j, k in enumerate(kinds):
+            per[k].append(e[j].elapsed_time(e[j + 1]) * 1e3)     # us
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    ms_step = elapsed / args.steps * 1e3
+    N = inp["Nmax"]
+    by = decode_bytes(sp, N)
+    dom = "indexer" if sp.kind == "decode" else "attend"
+    dom_bytes = by[dom] * sp.B
+    achieved = dom_bytes / (avg[dom] * 1e-6) / 1e9
+    value = sp.B * args.steps / elapsed
+    step_gbs = by["total"] * sp.B / (ms_step * 1e-3) / 1e9
+    res = dict(
+        metric=METRIC, value=value, unit="query-tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms_step, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype=("bf16" if sp.index_format == "bf16" else "mxfp4+fp8/bf16"),
+        data="synthetic",
+        config=dict(workload=sp.name, batch=sp.B, context=sp.L, compressed_entries=N, m=sp.m,
+                    heads=sp.nh, head_dim=sp.c, rope_dims=sp.d_r, top_k=sp.k or None,
+                    indexer=(f"{sp.nI}x{sp.cI} {sp.index_format}" if sp.nI else None),
+                    kv_format=sp.kv_format, window=sp.n_win, cache_copies=args.copies),
+        roofline=dict(bound="hbm", kernel=dom, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=achieved / HBM_PEAK_GBS, traffic=None,
+                      algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=avg[dom]),
+        step=dict(algorithmic_bytes=by["total"] * sp.B, achieved_gbs=step_gbs,
+                  frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS,
+                  kernel_us={k: round(v, 2) for k, v in avg.items()}),
+    )
+    return res, inp
+
+
+# ------------------------------------------------------------------ prefill bench
+def run_prefill(args, torch, I, G):
+    sp = I.CONFIGS[args.config]
+    dev = torch.device("cuda", 0)
+    t0 = time.perf_counter()
+    inp = I.prefill_inputs(sp)
+    print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        p = G.upload_prefill(inp, dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        G.prefill_compress(p, stream)
+        e1.record(stream)
+        G.prefill_attention_path(p, stream)
+    torch.cuda.synchronize()
+    t_comp = e0.elapsed_time(e1)
+    kinds = ["indexer", "topk", "attend"]
+    n = sp.T // sp.m
+    for _ in range(args.warmup):
+        with torch.cuda.stream(stream):
+            G.prefill_attention_path(p, stream)
+    torch.cuda.synchronize()
+    import long_context_sparse_10_amd as L
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    scale = 1.0 / math.sqrt(sp.c)
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            e = ev[i]
+            e[0].record(stream)
+            L.indexer_score(p.qI, None, L.BF16, p.w, p.kI, None, L.BF16, p.q_pos, p.n_entries, 1,
+                            sp.T, sp.nI, sp.cI, n, sp.m, p.scores, L.F32, stream)
+            e[1].record(stream)
+            L.topk_select(p.scores, L.F32, p.q_pos, p.n_entries, 1, sp.T, n, sp.m, sp.k, p.idx,
+                          None, stream)
+            e[2].record(stream)
+            L.sparse_mqa_attend(p.q, L.BF16, p.gamma, 1e-6, sp.d_r, 1e4, p.q_pos, p.kv, L.BF16, n,
+                                p.idx, sp.k, p.win, sp.T, sp.n_win, p.sink, scale, 1, sp.T, sp.nh,
+                                sp.c, p.out, L.BF16, p.ws_attend, stream)
+            e[3].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    avg = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) * 1e3
+           for j, k in enumerate(kinds)}
+    fi, fa = prefill_flops(sp, sp.T)
+    ms = elapsed / args.steps * 1e3
+    tflops = (fi + fa) / (ms * 1e-3) / 1e12
+    att = fa / (avg["attend"] * 1e-6) / 1e12
+    res = dict(
+        metric=METRIC, value=tflops, unit="TFLOP/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload=sp.name, seq_len=sp.T, hidden=sp.d, heads=sp.nh, head_dim=sp.c,
+                    top_k=sp.k, indexer=f"{sp.nI}x{sp.cI}", window=sp.n_win),
+        roofline=dict(bound="mfma", kernel="attend", achieved=att, peak=BF16_PEAK_TFLOPS,
+                      unit="TFLOP/s", frac=att / BF16_PEAK_TFLOPS, traffic=None,
+                      algorithmic_flops_per_launch=fa, avg_launch_us=avg["attend"]),
+        step=dict(indexer_tflops=fi / (avg["indexer"] * 1e-6) / 1e12,
+                  attend_tflops=att, kernel_us={k: round(v, 1) for k, v in avg.items()},
+                  compress_ms_untimed=t_comp),
+    )
+    return res, inp
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode_64k",
+                    choices=["decode_64k", "hca_decode_1m", "decode_1m_fp4", "prefill_32k"])
+    ap.add_argument("--copies", type=int, default=6, help="cache copies rotated (cold cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the decode batch shards by sequence; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import csa_inputs as I
+    from long_context_sparse_10_amd import pipeline as G
+    if args.config == "prefill_32k":
+        args.copies = 1
+        res, inp = run_prefill(args, torch, I, G)
+    else:
+        res, inp = run_decode(args, torch, I, G)
+    if not args.no_cpu_baseline:
+        if args.config == "prefill_32k":
+            rows = np.linspace(0, inp["T"] - 1, 64).astype(int)
+            res["cpu_baseline"] = cpu_baseline_prefill(inp, rows)
+        else:
+            res["cpu_baseline"] = cpu_baseline_decode(inp)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,10 +20,13 @@
  *    argument returns CSA_ERR_INVALID and launches nothing.  A dtype pairing the
  *    library has no kernel for returns CSA_ERR_UNSUPPORTED.  A launch failure
  *    returns CSA_ERR_LAUNCH.  No C++ exception crosses this boundary.
- *  - Workspace protocol (calls that take `ws`): with ws == NULL the call writes
- *    the bytes it needs to *ws_bytes and returns CSA_OK without launching;
- *    otherwise *ws_bytes must hold the size of `ws` and be at least that much
- *    (else CSA_ERR_WORKSPACE).  The size depends only on the host arguments.
+ *  - Workspace protocol (calls that take `ws`): with ws_bytes != NULL and
+ *    ws == NULL the call writes the bytes it needs to *ws_bytes and returns
+ *    CSA_OK without launching; with both non-NULL, *ws_bytes is the size of
+ *    `ws` and must be at least that much (else CSA_ERR_WORKSPACE); with
+ *    ws_bytes == NULL the caller offers no workspace, which is accepted when
+ *    the call needs none and is CSA_ERR_WORKSPACE otherwise.  The size depends
+ *    only on the host arguments.
  *  - Positions are zero-based.  A query at position q sees the compressed
  *    entries s < N(q) = min(n_entries, (q + 1) / m): an entry is visible once
  *    its whole block has been processed (strict block causality).

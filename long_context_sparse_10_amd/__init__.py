@@ -1,0 +1,17 @@
+"""MI355X (gfx950) Compressed Sparse Attention: a C-ABI HIP library (libcsa.so)
+and its thin Python binding.
+
+The five calls of the path -- ``csa_compress``, ``indexer_score``,
+``topk_select``, ``sparse_mqa_attend``, ``hca_attend`` -- plus the row encoder
+``csa_prep_rows`` are re-exported from :mod:`._lib` with torch tensors in place
+of device pointers.  See ``include/csa.h`` for the contract of each call.
+"""
+from ._lib import (  # noqa: F401
+    BF16, F32, FP8MIX, MXFP4, CsaError, LIB_PATH, csa_compress, csa_prep_rows, hca_attend,
+    indexer_score, lib, sparse_mqa_attend, status_string, topk_select, version,
+)
+
+
+def row_bytes(fmt: int, c: int, rope_dims: int = 0) -> int:
+    """Bytes of one stored row in format ``fmt`` (scales of MXFP4 excluded)."""
+    return {F32: 4 * c, BF16: 2 * c, FP8MIX: (c - rope_dims) + 2 * rope_dims, MXFP4: c // 2}[fmt]

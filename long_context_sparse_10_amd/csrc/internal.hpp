@@ -1,0 +1,70 @@
+// Host-side launch wrappers of the gfx950 kernels.  The entry points in api.hip
+// validate every argument before calling these; the launchers only size grids.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+// prep.hip / compress.hip -------------------------------------------------
+hipError_t launch_prep_rows(const void* x, csa_dtype x_t, int64_t rows, int c,
+                            const float* norm_w, float eps, int rope_dims, float rope_theta,
+                            const int32_t* pos, int rows_per_seq, int pos_stride, int pos_offset,
+                            void* out, uint8_t* out_scale, csa_dtype out_t, hipStream_t s);
+
+// C[M, N] (fp32) = A[M, K] * B[K, N]; A and B both f32 or both bf16, row-major
+hipError_t launch_gemm(const void* A, const void* Bm, csa_dtype t, float* C, int M, int N, int K,
+                       hipStream_t s);
+
+hipError_t launch_pool(const float* Ca, const float* Za, const float* Cb, const float* Zb,
+                       const float* bias_a, const float* bias_b, int B, int T, int m, int c,
+                       const float* norm_w, float eps, int rope_dims, float rope_theta,
+                       int pos_stride, int pos_offset, void* out, uint8_t* out_scale,
+                       csa_dtype out_t, hipStream_t s);
+
+// indexer.hip ---------------------------------------------------------------
+hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_t, const float* w,
+                          const void* kI, const uint8_t* kI_scale, const int32_t* q_pos,
+                          const int32_t* n_entries, int B, int Tq, int nI, int cI, int Nmax,
+                          int m, void* scores, csa_dtype score_t, hipStream_t s);
+
+// topk.hip --------------------------------------------------------------------
+hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_pos,
+                       const int32_t* n_entries, int B, int Tq, int Nmax, int m, int k,
+                       int32_t* idx, hipStream_t s);
+
+// attend.hip -------------------------------------------------------------------
+struct AttendArgs {
+  const void* q;
+  csa_dtype q_t;
+  const float* q_norm_w;
+  float eps;
+  int rope_dims;
+  float rope_theta;
+  const int32_t* q_pos;
+  const void* kv;
+  csa_dtype kv_t;
+  int Nmax;
+  const int32_t* idx;        // sparse: [B, Tq, k]; NULL for dense (HCA)
+  int k;
+  const int32_t* n_entries;  // dense only
+  int m_prime;               // dense only
+  const void* win;
+  int win_len;
+  int n_win;
+  const float* sink;
+  float scale;
+  int B, Tq, nh, c;
+  void* out;
+  csa_dtype out_t;
+};
+
+// workspace bytes the attention call needs for these host sizes
+size_t attend_workspace(const AttendArgs& a);
+hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s);
+
+}  // namespace csa

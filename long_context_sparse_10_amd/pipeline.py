@@ -1,0 +1,247 @@
+"""Device-side composition of the CSA calls for whole workloads.
+
+Uploads the seeded synthetic inputs, builds the caches with the library's own
+kernels (``csa_prep_rows`` / ``csa_compress``) and runs one step of the hot
+path: ``indexer_score`` -> ``topk_select`` -> ``sparse_mqa_attend`` for CSA,
+``hca_attend`` for HCA.  Every arithmetic step runs in libcsa; torch provides
+device memory and streams only.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as C
+
+ROPE_THETA = 10000.0
+EPS = 1e-6
+FMT = {"f32": C.F32, "bf16": C.BF16, "fp8mix": C.FP8MIX, "mxfp4": C.MXFP4}
+
+
+def _row_bytes(fmt, c, d_r):
+    return {C.F32: 4 * c, C.BF16: 2 * c, C.FP8MIX: (c - d_r) + 2 * d_r, C.MXFP4: c // 2}[fmt]
+
+
+def to_dev(x: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Upload an fp32 array holding values of ``dtype`` ("f32" / "bf16")."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def encode_rows(x: torch.Tensor, fmt: int, rows: int, c: int, *, norm_w=None, d_r=0,
+                pos=None, rows_per_seq=1, pos_stride=1, pos_offset=0, stream=None):
+    """Run ``csa_prep_rows`` on ``rows`` rows of ``x`` into a new buffer of
+    format ``fmt``; returns (rows tensor, scales or None)."""
+    out = torch.empty(rows * _row_bytes(fmt, c, d_r), dtype=torch.uint8, device=x.device)
+    sc = torch.empty(rows * (c // 32), dtype=torch.uint8, device=x.device) if fmt == C.MXFP4 else None
+    xt = C.BF16 if x.dtype == torch.bfloat16 else C.F32
+    C.csa_prep_rows(x, xt, rows, c, norm_w, EPS, d_r, ROPE_THETA, pos, rows_per_seq, pos_stride,
+                    pos_offset, out, sc, fmt, stream)
+    return out, sc
+
+
+# ============================================================ decode
+@dataclass
+class Decode:
+    spec: object
+    B: int
+    Nmax: int
+    q: torch.Tensor
+    q_pos: torch.Tensor
+    n_entries: torch.Tensor
+    sink: torch.Tensor
+    gamma: torch.Tensor
+    kv: torch.Tensor
+    win: torch.Tensor
+    kv_fmt: int
+    qI: Optional[torch.Tensor] = None
+    qI_scale: Optional[torch.Tensor] = None
+    kI: Optional[torch.Tensor] = None
+    kI_scale: Optional[torch.Tensor] = None
+    w: Optional[torch.Tensor] = None
+    index_fmt: int = C.BF16
+    score_fmt: int = C.F32
+    scores: Optional[torch.Tensor] = None
+    idx: Optional[torch.Tensor] = None
+    out: Optional[torch.Tensor] = None
+    ws: Optional[torch.Tensor] = None
+    extra: dict = field(default_factory=dict)
+
+
+def upload_decode(inp: dict, device="cuda", stream=None) -> Decode:
+    """Device buffers for one decode step: the compressed caches (RMSNorm +
+    RoPE at position m*i, stored in the config's KV format), the window ring
+    (RoPE at each slot's own position), index keys and the query side."""
+    sp = inp["spec"]
+    B, Nmax, c, d_r = sp.B, inp["Nmax"], sp.c, sp.d_r
+    kv_fmt = FMT[sp.kv_format]
+    gamma = torch.ones(c, dtype=torch.float32, device=device)
+    raw = torch.from_numpy(inp["kv_raw"]).to(device)
+    kv, _ = encode_rows(raw, kv_fmt, B * Nmax, c, norm_w=gamma, d_r=d_r, rows_per_seq=Nmax,
+                        pos_stride=sp.m, stream=stream)
+    del raw
+    wraw = torch.from_numpy(inp["win_raw"]).to(device)
+    wpos = torch.from_numpy(inp["win_pos"].reshape(-1)).to(device)
+    win, _ = encode_rows(wraw, kv_fmt, B * sp.n_win, c, norm_w=gamma, d_r=d_r, pos=wpos,
+                         stream=stream)
+    d = Decode(spec=sp, B=B, Nmax=Nmax, q=to_dev(inp["q"], sp.dtype, device),
+               q_pos=torch.from_numpy(inp["q_pos"]).to(device),
+               n_entries=torch.from_numpy(inp["n_entries"]).to(device),
+               sink=torch.from_numpy(inp["sink"]).to(device), gamma=gamma, kv=kv, win=win,
+               kv_fmt=kv_fmt)
+    d.out = torch.empty(B, 1, sp.nh, c, dtype=torch.bfloat16, device=device)
+    if sp.kind == "decode":
+        d.index_fmt = FMT[sp.index_format]
+        if d.index_fmt == C.MXFP4:
+            kraw = torch.from_numpy(inp["kI"]).to(device)
+            d.kI, d.kI_scale = encode_rows(kraw, C.MXFP4, B * Nmax, sp.cI, stream=stream)
+            del kraw
+            qraw = torch.from_numpy(inp["qI"]).to(device)
+            d.qI, d.qI_scale = encode_rows(qraw, C.MXFP4, B * sp.nI, sp.cI, stream=stream)
+            d.score_fmt = C.BF16
+        else:
+            d.kI = to_dev(inp["kI"], sp.index_format, device)
+            d.qI = to_dev(inp["qI"], sp.index_format, device)
+            d.score_fmt = C.F32
+        d.w = torch.from_numpy(inp["w"]).to(device)
+        sdt = torch.bfloat16 if d.score_fmt == C.BF16 else torch.float32
+        d.scores = torch.empty(B, 1, Nmax, dtype=sdt, device=device)
+        d.idx = torch.empty(B, 1, sp.k, dtype=torch.int32, device=device)
+    return d
+
+
+def decode_indexer(d: Decode, stream=None):
+    sp = d.spec
+    C.indexer_score(d.qI, d.qI_scale, d.index_fmt, d.w, d.kI, d.kI_scale, d.index_fmt, d.q_pos,
+                    d.n_entries, d.B, 1, sp.nI, sp.cI, d.Nmax, sp.m, d.scores, d.score_fmt, stream)
+
+
+def decode_topk(d: Decode, stream=None):
+    sp = d.spec
+    C.topk_select(d.scores, d.score_fmt, d.q_pos, d.n_entries, d.B, 1, d.Nmax, sp.m, sp.k, d.idx,
+                  None, stream)
+
+
+def decode_attend(d: Decode, idx=None, stream=None):
+    sp = d.spec
+    qt = C.BF16 if d.q.dtype == torch.bfloat16 else C.F32
+    scale = 1.0 / math.sqrt(sp.c)
+    if sp.kind == "hca_decode":
+        d.ws = C.hca_attend(d.q, qt, d.gamma, EPS, sp.d_r, ROPE_THETA, d.q_pos, d.kv, d.kv_fmt,
+                            d.Nmax, d.n_entries, sp.m, d.win, sp.n_win, sp.n_win, d.sink, scale,
+                            d.B, 1, sp.nh, sp.c, d.out, C.BF16, d.ws, stream)
+    else:
+        d.ws = C.sparse_mqa_attend(d.q, qt, d.gamma, EPS, sp.d_r, ROPE_THETA, d.q_pos, d.kv,
+                                   d.kv_fmt, d.Nmax, d.idx if idx is None else idx, sp.k, d.win,
+                                   sp.n_win, sp.n_win, d.sink, scale, d.B, 1, sp.nh, sp.c, d.out,
+                                   C.BF16, d.ws, stream)
+
+
+def decode_step(d: Decode, stream=None):
+    """One decode step of the hot path for every sequence of the batch."""
+    if d.spec.kind == "decode":
+        decode_indexer(d, stream)
+        decode_topk(d, stream)
+    decode_attend(d, stream=stream)
+
+
+# ============================================================ prefill
+@dataclass
+class Prefill:
+    spec: object
+    T: int
+    dt: int
+    H: torch.Tensor
+    W: dict
+    q: torch.Tensor
+    qI: Optional[torch.Tensor]
+    w: Optional[torch.Tensor]
+    q_pos: torch.Tensor
+    n_entries: torch.Tensor
+    sink: torch.Tensor
+    gamma: torch.Tensor
+    kv: Optional[torch.Tensor] = None
+    kI: Optional[torch.Tensor] = None
+    win: Optional[torch.Tensor] = None
+    scores: Optional[torch.Tensor] = None
+    idx: Optional[torch.Tensor] = None
+    out: Optional[torch.Tensor] = None
+    ws: Optional[torch.Tensor] = None
+    ws_attend: Optional[torch.Tensor] = None
+
+
+def upload_prefill(inp: dict, device="cuda") -> Prefill:
+    sp = inp["spec"]
+    T, dt = inp["T"], sp.dtype
+    names = [k for k in inp if k.startswith("W") or k.startswith("bias")]
+    W = {}
+    for k in names:
+        W[k] = to_dev(inp[k], dt, device) if k.startswith("W") else torch.from_numpy(inp[k]).to(device)
+    p = Prefill(spec=sp, T=T, dt=FMT[dt], H=to_dev(inp["H"], dt, device), W=W,
+                q=to_dev(inp["q"], dt, device),
+                qI=to_dev(inp["qI"], dt, device) if sp.nI else None,
+                w=torch.from_numpy(inp["w"]).to(device) if sp.nI else None,
+                q_pos=torch.from_numpy(inp["q_pos"]).to(device),
+                n_entries=torch.tensor([T // sp.m], dtype=torch.int32, device=device),
+                sink=torch.from_numpy(inp["sink"]).to(device),
+                gamma=torch.ones(sp.c, dtype=torch.float32, device=device))
+    return p
+
+
+def prefill_compress(p: Prefill, stream=None):
+    """Compress the sequence: main KV entries (RMSNorm + RoPE at m*i), index keys
+    (second compressor, no norm / RoPE) and per-token window rows (m = 1)."""
+    sp, T = p.spec, p.T
+    n = T // sp.m
+    kv_fmt = FMT[sp.kv_format]
+    dev = p.H.device
+    p.kv = torch.empty(max(n, 1) * _row_bytes(kv_fmt, sp.c, sp.d_r), dtype=torch.uint8, device=dev)
+    overlap = sp.m == 4
+    W = p.W
+    p.ws = C.csa_compress(p.H, p.dt, 1, T, sp.d, W["W_kv_a"], W["W_z_a"],
+                          W.get("W_kv_b"), W.get("W_z_b"), W["bias_a"], W.get("bias_b"), sp.m,
+                          int(overlap), sp.c, p.gamma, EPS, sp.d_r, ROPE_THETA, sp.m, 0, p.kv, None,
+                          kv_fmt, p.ws, stream)
+    if sp.nI:
+        ifmt = FMT[sp.index_format]
+        p.kI = torch.empty(max(n, 1) * _row_bytes(ifmt, sp.cI, 0), dtype=torch.uint8, device=dev)
+        p.ws = C.csa_compress(p.H, p.dt, 1, T, sp.d, W["WI_kv_a"], W["WI_z_a"], W["WI_kv_b"],
+                              W["WI_z_b"], W["biasI_a"], W["biasI_b"], sp.m, 1, sp.cI, None, EPS, 0,
+                              ROPE_THETA, sp.m, 0, p.kI, None, ifmt, p.ws, stream)
+    p.win = torch.empty(T * _row_bytes(kv_fmt, sp.c, sp.d_r), dtype=torch.uint8, device=dev)
+    p.ws = C.csa_compress(p.H, p.dt, 1, T, sp.d, W["W_win"], None, None, None, None, None, 1, 0,
+                          sp.c, p.gamma, EPS, sp.d_r, ROPE_THETA, 1, 0, p.win, None, kv_fmt, p.ws,
+                          stream)
+
+
+def prefill_attention_path(p: Prefill, stream=None):
+    """Indexer -> top-k -> sparse attention (CSA), or dense HCA attention."""
+    sp, T = p.spec, p.T
+    Tq = p.q_pos.numel()
+    n = max(T // sp.m, 1)
+    dev = p.H.device
+    scale = 1.0 / math.sqrt(sp.c)
+    if p.out is None:
+        p.out = torch.empty(1, Tq, sp.nh, sp.c, dtype=p.q.dtype, device=dev)
+    ot = C.BF16 if p.q.dtype == torch.bfloat16 else C.F32
+    kv_fmt = FMT[sp.kv_format]
+    if sp.nI:
+        ifmt = FMT[sp.index_format]
+        if p.scores is None:
+            p.scores = torch.empty(1, Tq, n, dtype=torch.float32, device=dev)
+            p.idx = torch.empty(1, Tq, sp.k, dtype=torch.int32, device=dev)
+        C.indexer_score(p.qI, None, ifmt, p.w, p.kI, None, ifmt, p.q_pos, p.n_entries, 1, Tq, sp.nI,
+                        sp.cI, n, sp.m, p.scores, C.F32, stream)
+        C.topk_select(p.scores, C.F32, p.q_pos, p.n_entries, 1, Tq, n, sp.m, sp.k, p.idx, None,
+                      stream)
+        p.ws_attend = C.sparse_mqa_attend(p.q, ot, p.gamma, EPS, sp.d_r, ROPE_THETA, p.q_pos, p.kv,
+                                          kv_fmt, n, p.idx, sp.k, p.win, T, sp.n_win, p.sink, scale,
+                                          1, Tq, sp.nh, sp.c, p.out, ot, p.ws_attend, stream)
+    else:
+        p.ws_attend = C.hca_attend(p.q, ot, p.gamma, EPS, sp.d_r, ROPE_THETA, p.q_pos, p.kv, kv_fmt,
+                                   n, p.n_entries, sp.m, p.win, T, sp.n_win, p.sink, scale, 1, Tq,
+                                   sp.nh, sp.c, p.out, ot, p.ws_attend, stream)

@@ -1,0 +1,171 @@
+"""Host-side checks of libcsa's C ABI (CPU only: nothing here launches a kernel).
+
+The library must load, export every entry point include/csa.h declares, and
+reject bad arguments on the host before any launch.  Pointers passed below are
+dummies that are never dereferenced: every call either fails validation or is a
+pure workspace-size query."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sparse_10_amd as L
+from long_context_sparse_10_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+D = 4096          # dummy non-null "device pointer", never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"^(?:csa_status|const char\*)\s+(\w+)\(", src, flags=re.M)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = L.lib()
+    names = declared_functions()
+    assert set(names) == {"csa_version", "csa_status_string", "csa_prep_rows", "csa_compress",
+                          "indexer_score", "topk_select", "sparse_mqa_attend", "hca_attend"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+    assert "gfx950" in L.version()
+
+
+def _prep(**kw):
+    a = dict(x=D, x_t=L.F32, rows=10, c=64, norm_w=None, eps=1e-6, rope_dims=16, theta=1e4,
+             pos=None, rps=1, ps=1, po=0, out=D, out_scale=None, out_t=L.BF16)
+    a.update(kw)
+    return L.lib().csa_prep_rows(a["x"], a["x_t"], a["rows"], a["c"], a["norm_w"], a["eps"],
+                                 a["rope_dims"], a["theta"], a["pos"], a["rps"], a["ps"], a["po"],
+                                 a["out"], a["out_scale"], a["out_t"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x_t=L.MXFP4), _lib.ERR_UNSUPPORTED),
+    (dict(out_t=7), _lib.ERR_UNSUPPORTED),
+    (dict(c=63), _lib.ERR_INVALID),
+    (dict(rope_dims=66), _lib.ERR_INVALID),
+    (dict(rope_dims=15), _lib.ERR_INVALID),
+    (dict(x=None), _lib.ERR_INVALID),
+    (dict(out=None), _lib.ERR_INVALID),
+    (dict(rows=-1), _lib.ERR_INVALID),
+    (dict(rps=0), _lib.ERR_INVALID),
+    (dict(out_t=L.MXFP4, c=48, out_scale=D), _lib.ERR_INVALID),
+    (dict(out_t=L.MXFP4, out_scale=None), _lib.ERR_INVALID),
+    (dict(out_t=L.FP8MIX, rope_dims=0), _lib.ERR_INVALID),
+    (dict(theta=0.0), _lib.ERR_INVALID),
+    (dict(eps=-1.0), _lib.ERR_INVALID),
+    (dict(rows=0), _lib.OK),            # nothing to do: no launch
+])
+def test_prep_rows_validation(kw, want):
+    assert _prep(**kw) == want
+
+
+def _compress(ws=None, ws_bytes=None, **kw):
+    a = dict(H=D, h_t=L.BF16, B=1, T=64, d=32, kva=D, za=D, kvb=D, zb=D, ba=D, bb=D, m=4, ov=1,
+             c=64, norm=None, eps=1e-6, rd=16, th=1e4, ps=4, po=0, out=D, osc=None, out_t=L.BF16)
+    a.update(kw)
+    return L.lib().csa_compress(a["H"], a["h_t"], a["B"], a["T"], a["d"], a["kva"], a["za"],
+                                a["kvb"], a["zb"], a["ba"], a["bb"], a["m"], a["ov"], a["c"],
+                                a["norm"], a["eps"], a["rd"], a["th"], a["ps"], a["po"], a["out"],
+                                a["osc"], a["out_t"], ws, ws_bytes, None)
+
+
+def test_compress_validation_and_workspace():
+    need = ctypes.c_size_t(0)
+    assert _compress(ws_bytes=ctypes.byref(need)) == _lib.OK
+    assert need.value == 64 * 64 * 4 * 4           # four fp32 [T, c] projections
+    need1 = ctypes.c_size_t(0)
+    assert _compress(ws_bytes=ctypes.byref(need1), za=None, kvb=None, zb=None, ba=None, bb=None,
+                     m=1, ov=0) == _lib.OK
+    assert need1.value == 64 * 64 * 4
+    small = ctypes.c_size_t(16)
+    assert _compress(ws=D, ws_bytes=ctypes.byref(small)) == _lib.ERR_WORKSPACE
+    assert _compress(ws=D, ws_bytes=None) == _lib.ERR_WORKSPACE
+    assert _compress(za=None) == _lib.ERR_INVALID                      # m = 4 needs gates
+    assert _compress(kvb=None) == _lib.ERR_INVALID                     # overlap needs b-series
+    assert _compress(ov=0) == _lib.ERR_INVALID                         # b-series without overlap
+    assert _compress(h_t=L.FP8MIX) == _lib.ERR_UNSUPPORTED
+    assert _compress(T=0) == _lib.ERR_INVALID
+
+
+def _indexer(**kw):
+    a = dict(qI=D, qs=None, qt=L.BF16, w=D, kI=D, ks=None, kt=L.BF16, qp=D, ne=D, B=2, Tq=1, nI=64,
+             cI=128, N=100, m=4, sc=D, st=L.F32)
+    a.update(kw)
+    return L.lib().indexer_score(a["qI"], a["qs"], a["qt"], a["w"], a["kI"], a["ks"], a["kt"],
+                                 a["qp"], a["ne"], a["B"], a["Tq"], a["nI"], a["cI"], a["N"],
+                                 a["m"], a["sc"], a["st"], None)
+
+
+def test_indexer_validation():
+    assert _indexer(kt=L.F32) == _lib.ERR_UNSUPPORTED
+    assert _indexer(qt=L.FP8MIX, kt=L.FP8MIX) == _lib.ERR_UNSUPPORTED
+    assert _indexer(st=L.MXFP4) == _lib.ERR_UNSUPPORTED
+    assert _indexer(qt=L.MXFP4, kt=L.MXFP4) == _lib.ERR_INVALID          # scales missing
+    assert _indexer(qt=L.MXFP4, kt=L.MXFP4, qs=D, ks=D, cI=48) == _lib.ERR_INVALID
+    assert _indexer(w=None) == _lib.ERR_INVALID
+    assert _indexer(m=0) == _lib.ERR_INVALID
+    assert _indexer(N=0) == _lib.ERR_INVALID
+    assert _indexer(B=0) == _lib.OK                                         # empty batch
+
+
+def test_topk_validation_and_workspace():
+    f = L.lib().topk_select
+    need = ctypes.c_size_t(99)
+    assert f(D, L.F32, D, D, 2, 1, 100, 4, 8, D, None, ctypes.byref(need), None) == _lib.OK
+    assert need.value == 0
+    assert f(D, L.F32, D, D, 2, 1, 100, 4, 0, D, None, None, None) == _lib.ERR_INVALID
+    assert f(D, L.FP8MIX, D, D, 2, 1, 100, 4, 8, D, None, None, None) == _lib.ERR_UNSUPPORTED
+    assert f(None, L.F32, D, D, 2, 1, 100, 4, 8, D, None, None, None) == _lib.ERR_INVALID
+    assert f(D, L.F32, D, D, 0, 1, 100, 4, 8, D, None, None, None) == _lib.OK
+
+
+def _attend(sparse=True, ws=None, ws_bytes=None, **kw):
+    a = dict(q=D, qt=L.BF16, qn=None, eps=1e-6, rd=64, th=1e4, qp=D, kv=D, kvt=L.BF16, N=16384,
+             idx=D, k=1024, ne=D, mp=128, win=D, wl=128, nw=128, sink=D, scale=0.044, B=32, Tq=1,
+             nh=64, c=512, out=D, ot=L.BF16)
+    a.update(kw)
+    if sparse:
+        return L.lib().sparse_mqa_attend(a["q"], a["qt"], a["qn"], a["eps"], a["rd"], a["th"],
+                                         a["qp"], a["kv"], a["kvt"], a["N"], a["idx"], a["k"],
+                                         a["win"], a["wl"], a["nw"], a["sink"], a["scale"], a["B"],
+                                         a["Tq"], a["nh"], a["c"], a["out"], a["ot"], ws, ws_bytes,
+                                         None)
+    return L.lib().hca_attend(a["q"], a["qt"], a["qn"], a["eps"], a["rd"], a["th"], a["qp"],
+                              a["kv"], a["kvt"], a["N"], a["ne"], a["mp"], a["win"], a["wl"],
+                              a["nw"], a["sink"], a["scale"], a["B"], a["Tq"], a["nh"], a["c"],
+                              a["out"], a["ot"], ws, ws_bytes, None)
+
+
+def test_attend_validation():
+    assert _attend(win=None) == _lib.ERR_INVALID
+    assert _attend(wl=64) == _lib.ERR_INVALID                 # ring shorter than the window
+    assert _attend(idx=None) == _lib.ERR_INVALID
+    assert _attend(k=0) == _lib.ERR_INVALID
+    assert _attend(kvt=L.FP8MIX, rd=0) == _lib.ERR_INVALID
+    assert _attend(kvt=L.MXFP4) == _lib.ERR_UNSUPPORTED
+    assert _attend(qt=L.FP8MIX) == _lib.ERR_UNSUPPORTED
+    assert _attend(sparse=False, ne=None) == _lib.ERR_INVALID
+    assert _attend(sparse=False, mp=0) == _lib.ERR_INVALID
+    assert _attend(rd=63) == _lib.ERR_INVALID
+    assert _attend(sink=None) == _lib.ERR_INVALID
+
+
+def test_attend_workspace_depends_on_slots_not_batch():
+    """Split partials are sized per query row; the split plan is a function of
+    the slot count only, so the per-row size is the same at any batch size."""
+    sizes = []
+    for B in (1, 8, 32):
+        need = ctypes.c_size_t(0)
+        assert _attend(B=B, ws_bytes=ctypes.byref(need)) == _lib.OK
+        sizes.append(need.value / B)
+    assert sizes[0] == sizes[1] == sizes[2] > 0
+    need = ctypes.c_size_t(0)
+    assert _attend(Tq=4096, B=1, ws_bytes=ctypes.byref(need)) == _lib.OK
+    assert need.value == 0                                    # many query rows: no split
+    small = ctypes.c_size_t(1)
+    assert _attend(ws=D, ws_bytes=ctypes.byref(small)) == _lib.ERR_WORKSPACE

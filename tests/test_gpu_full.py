@@ -1,0 +1,135 @@
+"""Full-size parity: the workloads ``bench.py`` times, in the same launch
+configuration, checked on sampled sequences / query rows the oracle computes
+one by one.  Top-k sets must be bit-exact wherever the oracle's k-th and
+(k+1)-th scores are further apart than the fp32 error bound; elsewhere the GPU
+set must be a valid top-k of the oracle's scores within that bound."""
+import numpy as np
+import pytest
+import torch
+
+import csa_inputs as I
+from long_context_sparse_10_amd import pipeline as G
+from oracle import csa as O
+from oracle import pipeline as OP
+from tests.gpu_util import bf16_ulp, dev, np64, report, score_error_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def check_topk(got, scores, nv, k, bound):
+    """Returns True when the set is bit-exact; asserts validity otherwise."""
+    want = O.topk(scores, nv, k)
+    if np.array_equal(got, want):
+        return True
+    sel = got[got >= 0]
+    assert sel.size == min(k, nv) and np.all(np.diff(sel) > 0) and np.all(got[sel.size:] == -1)
+    assert not OP.tie_free(scores, nv, k, 2 * bound), "tie-free query selected a different set"
+    mask = np.zeros(nv, bool)
+    mask[sel] = True
+    assert scores[mask].min() >= scores[~mask].max() - 2 * bound
+    return False
+
+
+def _decode_full(name, seqs):
+    d = dev()
+    sp = I.CONFIGS[name]
+    inp = I.decode_inputs(sp)
+    print(f"[full] {name}: inputs ready", flush=True)
+    g = G.upload_decode(inp, d)
+    G.decode_step(g)
+    torch.cuda.synchronize()
+    print(f"[full] {name}: GPU step done", flush=True)
+    return sp, inp, g
+
+
+def test_decode_64k_full():
+    sp, inp, g = _decode_full("decode_64k", None)
+    S, idx, out = np64(g.scores), g.idx.cpu().numpy(), np64(g.out)
+    exact = 0
+    for b in (0, 13, 31):
+        ref = OP.decode_reference(inp, b)
+        nv = ref["n_vis"]
+        bound = score_error_bound(inp["qI"][b, 0], inp["w"][b, 0], inp["kI"][b], nv)
+        assert np.all(np.abs(S[b, 0, :nv] - ref["scores"]) <= bound)
+        same = check_topk(idx[b, 0], ref["scores"], nv, sp.k, bound.max())
+        exact += same
+        want = ref["out"] if same else OP.decode_attend(inp, b, idx[b, 0])
+        err = np.abs(out[b, 0] - want).max()
+        report("decode_64k", b=b, idx_exact=same, max_abs=err)
+        assert err <= 2e-2
+    assert exact >= 1
+
+
+def test_hca_decode_1m_full():
+    sp, inp, g = _decode_full("hca_decode_1m", None)
+    out = np64(g.out)
+    for b in (0, 15):
+        want = OP.decode_attend(inp, b, None)
+        err = np.abs(out[b, 0] - want).max()
+        report("hca_decode_1m", b=b, max_abs=err)
+        assert err <= 2e-2
+
+
+def test_decode_1m_fp4_full():
+    """MXFP4 index keys + FP8/BF16 KV at 262,144 entries: scores within one
+    bf16 step of the quantised oracle, top-k valid against it (bit-exact where
+    tie-free), attention within 2e-2; recall against the unquantised fp64
+    oracle is reported (parity unpinned: the pages' 99.7% is a trained-model
+    figure)."""
+    sp, inp, g = _decode_full("decode_1m_fp4", None)
+    S, idx, out = np64(g.scores), g.idx.cpu().numpy(), np64(g.out)
+    for b in (0, 7):
+        ref = OP.decode_reference(inp, b)
+        nv = ref["n_vis"]
+        ulp = bf16_ulp(ref["scores"])
+        assert np.all(np.abs(S[b, 0, :nv] - ref["scores"]) <= ulp)
+        same = check_topk(idx[b, 0], ref["scores"], nv, sp.k, float(ulp.max()))
+        want = ref["out"] if same else OP.decode_attend(inp, b, idx[b, 0])
+        err = np.abs(out[b, 0] - want).max()
+        exact_scores = O.index_scores(inp["qI"][b, 0], inp["w"][b, 0], inp["kI"][b], nv)
+        ref_set = set(O.topk(exact_scores, nv, sp.k).tolist())
+        recall = len(ref_set & set(idx[b, 0].tolist())) / sp.k
+        report("decode_1m_fp4", b=b, idx_exact_vs_quantised=same, max_abs=err,
+               recall_vs_fp64=recall)
+        assert err <= 2e-2
+
+
+def test_prefill_32k_full():
+    """The whole prefill on the GPU (compression included), oracle on sampled
+    query rows: causal boundaries, first window, middle and the last query."""
+    d = dev()
+    sp = I.CONFIGS["prefill_32k"]
+    inp = I.prefill_inputs(sp)
+    p = G.upload_prefill(inp, d)
+    G.prefill_compress(p)
+    G.prefill_attention_path(p)
+    torch.cuda.synchronize()
+    print("[full] prefill_32k: GPU done", flush=True)
+    caches = OP.prefill_caches(inp)
+    print("[full] prefill_32k: oracle caches done", flush=True)
+    rows = [0, 3, 4, 7, 8, 127, 128, 4095, 4096, 4099, 16383, 20000, 32766, 32767]
+    refs = OP.prefill_reference(inp, caches, rows)
+    S = p.scores[0]
+    exact = 0
+    for r, ref in zip(rows, refs):
+        nv = ref["n_vis"]
+        got_idx = p.idx[0, r].cpu().numpy()
+        srow = S[r, :nv].double().cpu().numpy()
+        bound = score_error_bound(inp["qI"][r], inp["w"][r], caches["kI"], nv)
+        # the GPU scores use the GPU's own bf16 index keys; compare within the
+        # bf16 storage of the keys plus fp32 accumulation
+        kb = score_error_bound(inp["qI"][r], inp["w"][r], caches["kI_exact"], nv, rel=2 ** -8)
+        assert np.all(np.abs(srow - ref["scores"]) <= bound + kb + 1e-6)
+        same = check_topk(got_idx, ref["scores"], nv, sp.k, float((bound + kb).max()) if nv else 0)
+        exact += same
+        out = p.out[0, r].double().cpu().numpy()
+        if same:
+            err = np.abs(out - ref["out"]).max()
+        else:
+            X = O.gather_rows(caches["kv"], got_idx, caches["win"], ref["pos"], sp.n_win, sp.T)
+            want = O.attend_query(inp["q"][r], None, 1e-6, sp.d_r, 1e4, ref["pos"], X, inp["sink"],
+                                  1 / np.sqrt(sp.c))
+            err = np.abs(out - want).max()
+        report("prefill_32k", row=r, n_vis=nv, idx_exact=same, max_abs=err)
+        assert err <= 2e-2
+    report("prefill_32k", rows=len(rows), idx_exact=exact)

@@ -1,0 +1,301 @@
+"""Stage-by-stage parity of the HIP path against the fp64 oracle, at sizes the
+oracle finishes in seconds that still span several tiles and ragged tails.
+Every call goes through the C ABI (ctypes binding); both sides consume the same
+seeded raw inputs and each side does its own normalisation, RoPE and encoding."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import csa_inputs as I
+import long_context_sparse_10_amd as L
+from long_context_sparse_10_amd import pipeline as G
+from oracle import csa as O
+from oracle import formats as F
+from oracle import pipeline as OP
+from tests.gpu_util import (bf16_ulp, decode_rows, dev, e4m3_ulp, np64, report,
+                            score_error_bound)
+
+pytestmark = pytest.mark.gpu
+
+
+# =================================================================== row encoder
+@pytest.mark.parametrize("c,d_r", [(512, 64), (64, 16)])
+def test_prep_rows_norm_rope_formats(c, d_r):
+    d = dev()
+    rng = np.random.default_rng(100)
+    rows = 777
+    raw = rng.standard_normal((rows, c), dtype=np.float32) * 3
+    pos = rng.integers(0, 1 << 20, rows).astype(np.int32)
+    ref = O.rope(O.rms_norm(raw, None, 1e-6), pos, d_r)
+    x = torch.from_numpy(raw).to(d)
+    p = torch.from_numpy(pos).to(d)
+    g = torch.ones(c, device=d)
+    fmts = [L.F32, L.BF16] + ([L.FP8MIX] if c == 512 else [])
+    for fmt in fmts:
+        out, _ = G.encode_rows(x, fmt, rows, c, norm_w=g, d_r=d_r, pos=p)
+        torch.cuda.synchronize()
+        got = decode_rows(out, fmt, rows, c, d_r)
+        if fmt == L.F32:
+            err = np.abs(got - ref).max()
+            report("prep f32", c=c, max_abs=err)
+            assert err < 2e-5
+            continue
+        want = OP.store(ref, "bf16" if fmt == L.BF16 else "fp8mix", d_r)
+        ulp = bf16_ulp(ref) if fmt == L.BF16 else np.concatenate(
+            [e4m3_ulp(ref[:, : c - d_r]), bf16_ulp(ref[:, c - d_r:])], 1)
+        mism = got != want
+        report("prep", fmt=fmt, c=c, mismatches=int(mism.sum()), of=got.size)
+        # a stored value may differ from the oracle's only by one step, and only
+        # where the exact value sits within fp32 error of a rounding midpoint
+        assert np.all(np.abs(got - ref) <= ulp * 0.5 + 1e-5 * np.abs(ref) + 1e-12)
+        assert mism.mean() < 1e-3
+
+
+def test_prep_rows_mxfp4_bit_exact():
+    """Pure MXFP4 encoding of fp32 values is byte work: codes and scales must be
+    bit-identical to the oracle's quantiser."""
+    d = dev()
+    rng = np.random.default_rng(101)
+    rows, c = 1000, 128
+    raw = rng.standard_normal((rows, c), dtype=np.float32)
+    raw[3] = 0.0                                     # all-zero blocks
+    raw[4, :32] = np.float32(6.0)                   # exact grid values
+    raw[5, :32] = rng.standard_normal(32).astype(np.float32) * 1e-30
+    out, sc = G.encode_rows(torch.from_numpy(raw).to(d), L.MXFP4, rows, c)
+    packed, scales = F.mxfp4_quantize(raw.astype(np.float64))
+    np.testing.assert_array_equal(out.cpu().numpy().reshape(rows, c // 2), packed)
+    np.testing.assert_array_equal(sc.cpu().numpy().reshape(rows, c // 32), scales)
+
+
+# =================================================================== compressor
+@pytest.mark.parametrize("name", ["tiny_csa", "tiny_hca"])
+def test_compress_tiny_f32(name):
+    d = dev()
+    sp = I.CONFIGS[name]
+    inp = I.prefill_inputs(sp)
+    p = G.upload_prefill(inp, d)
+    G.prefill_compress(p)
+    torch.cuda.synchronize()
+    ref = OP.prefill_caches(inp)
+    n = sp.T // sp.m
+    kv = decode_rows(p.kv, L.F32, n, sp.c, sp.d_r)
+    win = decode_rows(p.win, L.F32, sp.T, sp.c, sp.d_r)
+    e1, e2 = np.abs(kv - ref["kv"]).max(), np.abs(win - ref["win"]).max()
+    report("compress", cfg=name, kv=e1, win=e2)
+    assert e1 <= 1e-5 and e2 <= 1e-5
+    if sp.nI:
+        kI = decode_rows(p.kI, L.F32, n, sp.cI, 0)
+        e3 = np.abs(kI - ref["kI"]).max()
+        report("compress", cfg=name, index_keys=e3)
+        assert e3 <= 1e-5
+
+
+def test_compress_bf16_mfma_gemm():
+    """bf16 hidden / weights (the prefill workload's dims, shorter sequence):
+    the MFMA projection + pooling + norm + RoPE.  Stored bf16 the entries must
+    sit within the bf16 bar (max-abs 2e-2) of the exact fp64 values; stored fp32
+    the same kernels must agree to fp32-accumulation accuracy."""
+    d = dev()
+    sp = I.CONFIGS["prefill_32k"]
+    T = 520                                            # 130 entries, ragged vs 128-row tiles
+    inp = I.prefill_inputs(sp, T=T, queries=np.arange(4))
+    p = G.upload_prefill(inp, d)
+    G.prefill_compress(p)
+    torch.cuda.synchronize()
+    ref = OP.prefill_caches(inp)
+    n = T // 4
+    kv = decode_rows(p.kv, L.BF16, n, sp.c, sp.d_r)
+    exact = O.compress(inp["H"], inp["W_kv_a"], inp["W_z_a"], inp["bias_a"], 4, inp["W_kv_b"],
+                       inp["W_z_b"], inp["bias_b"], None, 1e-6, sp.d_r, 1e4, 4, 0)
+    err = np.abs(kv - exact)
+    mism = float((kv != ref["kv"]).mean())
+    report("compress bf16", max_abs=err.max(), mism=mism)
+    assert err.max() <= 2e-2 and mism < 1e-2
+    kI = decode_rows(p.kI, L.BF16, n, sp.cI, 0)
+    assert np.abs(kI - ref["kI_exact"]).max() <= 2e-2
+    win = decode_rows(p.win, L.BF16, T, sp.c, sp.d_r)
+    assert np.abs(win - ref["win"]).max() <= 2e-2
+    # fp32 output of the same bf16 inputs isolates the kernels' own arithmetic
+    out32 = torch.empty(n * sp.c * 4, dtype=torch.uint8, device=d)
+    W = p.W
+    L.csa_compress(p.H, L.BF16, 1, T, sp.d, W["W_kv_a"], W["W_z_a"], W["W_kv_b"], W["W_z_b"],
+                   W["bias_a"], W["bias_b"], 4, 1, sp.c, p.gamma, 1e-6, sp.d_r, 1e4, 4, 0, out32,
+                   None, L.F32)
+    torch.cuda.synchronize()
+    e32 = np.abs(decode_rows(out32, L.F32, n, sp.c, sp.d_r) - exact).max()
+    report("compress bf16->f32", max_abs=e32)
+    assert e32 <= 2e-3
+
+
+# =================================================================== indexer
+def _decode_small(name, B, lengths, seed):
+    sp = I.CONFIGS[name].replace(B=B)
+    return I.decode_inputs(sp, seed=seed, lengths=lengths)
+
+
+@pytest.mark.parametrize("lengths", [[4100, 2051, 8191], [64, 3, 4099]])
+def test_indexer_bf16_mfma(lengths):
+    d = dev()
+    inp = _decode_small("decode_64k", len(lengths), lengths, 200)
+    g = G.upload_decode(inp, d)
+    g.scores.fill_(float("nan"))
+    G.decode_indexer(g)
+    torch.cuda.synchronize()
+    S = np64(g.scores)
+    for b in range(len(lengths)):
+        ref, nv = OP.decode_scores(inp, b)
+        bound = score_error_bound(inp["qI"][b, 0], inp["w"][b, 0], inp["kI"][b], nv)
+        err = np.abs(S[b, 0, :nv] - ref)
+        report("indexer bf16", b=b, nv=nv, max_err=err.max() if nv else 0)
+        assert np.all(err <= bound + 1e-30)
+        assert np.all(np.isnan(S[b, 0, nv:]))          # invisible entries untouched
+
+
+def test_indexer_mxfp4_matches_quantized_oracle():
+    d = dev()
+    inp = _decode_small("decode_1m_fp4", 2, [4 * 3000 + 3, 4 * 777], 201)
+    g = G.upload_decode(inp, d)
+    G.decode_indexer(g)
+    torch.cuda.synchronize()
+    S = np64(g.scores)
+    # the encoded keys are byte-identical to the oracle's quantiser
+    packed, scales = F.mxfp4_quantize(inp["kI"].astype(np.float64))
+    Nm = inp["Nmax"]
+    np.testing.assert_array_equal(g.kI.cpu().numpy().reshape(2, Nm, 64), packed)
+    np.testing.assert_array_equal(g.kI_scale.cpu().numpy().reshape(2, Nm, 4), scales)
+    for b in range(2):
+        ref, nv = OP.decode_scores(inp, b)          # quantised fp64 scores, rounded to bf16
+        err = np.abs(S[b, 0, :nv] - ref)
+        ulp = bf16_ulp(ref)
+        report("indexer mxfp4", b=b, nv=nv, ulps=float((err / ulp).max()))
+        assert np.all(err <= ulp + 1e-30)
+
+
+def test_indexer_generic_f32_and_causal_prefill():
+    d = dev()
+    sp = I.CONFIGS["tiny_csa"]
+    inp = I.prefill_inputs(sp)
+    p = G.upload_prefill(inp, d)
+    G.prefill_compress(p)
+    n = sp.T // 4
+    scores = torch.full((1, sp.T, n), float("nan"), device=d)
+    L.indexer_score(p.qI, None, L.F32, p.w, p.kI, None, L.F32, p.q_pos, p.n_entries, 1, sp.T,
+                    sp.nI, sp.cI, n, 4, scores, L.F32)
+    torch.cuda.synchronize()
+    S = np64(scores)[0]
+    ref = OP.prefill_caches(inp)
+    worst = 0.0
+    for t in range(0, sp.T, 7):
+        nv = (t + 1) // 4
+        want = O.index_scores(inp["qI"][t], inp["w"][t], ref["kI"], nv)
+        bound = score_error_bound(inp["qI"][t], inp["w"][t], ref["kI"], nv, rel=1e-4)
+        assert np.all(np.abs(S[t, :nv] - want) <= bound + 1e-5)
+        assert np.all(np.isnan(S[t, nv:]))
+        if nv:
+            worst = max(worst, float(np.abs(S[t, :nv] - want).max()))
+    report("indexer f32 causal", max_err=worst)
+
+
+# =================================================================== top-k
+def _score_rows(rng, kind, rows, N):
+    if kind == "ties":
+        return rng.integers(-4, 5, size=(rows, N)).astype(np.float32)
+    if kind == "bf16":
+        return I.cast(rng.standard_normal((rows, N)).astype(np.float32) * 0.5, "bf16")
+    return rng.standard_normal((rows, N)).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["ties", "bf16", "normal"])
+@pytest.mark.parametrize("N,k,m", [(16384, 1024, 4), (3000, 1024, 4), (700, 32, 4),
+                                   (1025, 1024, 4), (40000, 512, 4)])
+def test_topk_bit_exact(kind, N, k, m):
+    """Same score arrays (from the seeded generator) on both sides: the index
+    sets are integer results and must be identical, ties included."""
+    d = dev()
+    rng = np.random.default_rng(N + k)
+    rows = 6
+    S = _score_rows(rng, kind, rows, N)
+    # query positions: full, ragged, tiny (N(q) <= k), empty
+    qpos = np.array([4 * N - 1, 4 * N - 3, 4 * (N // 3) + 2, 4 * k + 1, 4 * k + 7, 2], np.int32)
+    n_ent = np.full(rows, N, np.int32)
+    fmt = L.BF16 if kind == "bf16" else L.F32
+    dt = torch.bfloat16 if fmt == L.BF16 else torch.float32
+    st = torch.from_numpy(S).to(d).to(dt).reshape(rows, 1, N)
+    idx = torch.empty(rows, 1, k, dtype=torch.int32, device=d)
+    L.topk_select(st, fmt, torch.from_numpy(qpos).reshape(rows, 1).to(d),
+                  torch.from_numpy(n_ent).to(d), rows, 1, N, m, k, idx)
+    got = idx.cpu().numpy()[:, 0]
+    for r in range(rows):
+        nv = int(O.n_visible(int(qpos[r]), m, N))
+        want = O.topk(S[r].astype(np.float64), nv, k)
+        np.testing.assert_array_equal(got[r], want, err_msg=f"row {r} nv {nv}")
+
+
+# =================================================================== attention
+def _attend_case(name, lengths, seed, holes=0.1, n_win=None):
+    sp = I.CONFIGS[name].replace(B=len(lengths))
+    if n_win is not None:
+        sp = sp.replace(n_win=n_win)
+    inp = I.decode_inputs(sp, seed=seed, lengths=lengths)
+    rng = np.random.default_rng(seed + 1)
+    nv = np.array([O.n_visible(int(inp["q_pos"][b, 0]), sp.m, int(inp["n_entries"][b]))
+                   for b in range(sp.B)])
+    idx = I.random_index_sets(rng, nv, sp.k, holes=holes) if sp.kind == "decode" else None
+    return sp, inp, idx
+
+
+@pytest.mark.parametrize("name,lengths", [
+    ("decode_64k", [4100, 9000, 300]),           # bf16 KV, 64 heads, split path
+    ("decode_1m_fp4", [8192 + 5, 5000]),          # FP8/BF16 KV, 128 heads (two head groups)
+    ("hca_decode_1m", [128 * 300 + 5, 128 * 40, 100]),  # dense HCA, bf16
+])
+def test_attend_decode_vs_oracle(name, lengths):
+    d = dev()
+    sp, inp, idx = _attend_case(name, lengths, 300)
+    g = G.upload_decode(inp, d)
+    idx_t = torch.from_numpy(idx).reshape(sp.B, 1, sp.k).to(d) if idx is not None else None
+    G.decode_attend(g, idx=idx_t)
+    torch.cuda.synchronize()
+    out = np64(g.out)
+    for b in range(sp.B):
+        want = OP.decode_attend(inp, b, idx[b] if idx is not None else None)
+        err = np.abs(out[b, 0] - want).max()
+        report("attend", cfg=name, b=b, max_abs=err)
+        assert err <= 2e-2
+
+
+def test_attend_window_edges_and_empty_selection():
+    """Window crossing position 0, all-empty selections (window only), one row."""
+    d = dev()
+    sp, inp, _ = _attend_case("decode_64k", [1, 5, 130, 4096], 310)
+    idx = np.full((sp.B, sp.k), -1, np.int32)
+    idx[3, :7] = np.arange(7) * 100
+    g = G.upload_decode(inp, d)
+    G.decode_attend(g, idx=torch.from_numpy(idx).reshape(sp.B, 1, sp.k).to(d))
+    torch.cuda.synchronize()
+    out = np64(g.out)
+    for b in range(sp.B):
+        want = OP.decode_attend(inp, b, idx[b])
+        assert np.abs(out[b, 0] - want).max() <= 2e-2
+
+
+def test_attend_deterministic_and_batch_invariant():
+    d = dev()
+    sp, inp, idx = _attend_case("decode_64k", [4100, 9000, 300], 320)
+    g = G.upload_decode(inp, d)
+    it = torch.from_numpy(idx).reshape(sp.B, 1, sp.k).to(d)
+    G.decode_attend(g, idx=it)
+    a = g.out.clone()
+    G.decode_attend(g, idx=it)
+    assert torch.equal(a, g.out)
+    # sequence 1 alone gives the same bits as inside the batch
+    one = {k: (v[1:2] if isinstance(v, np.ndarray) and v.ndim and v.shape[0] == sp.B else v)
+           for k, v in inp.items()}
+    one["spec"] = sp.replace(B=1)
+    one["Nmax"] = inp["Nmax"]
+    g1 = G.upload_decode(one, d)
+    G.decode_attend(g1, idx=it[1:2].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(g1.out[0], a[1])
