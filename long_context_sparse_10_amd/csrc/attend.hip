@@ -73,7 +73,7 @@ __device__ __forceinline__ SlotCtx make_ctx(const AttendArgs& a, int row) {
 
 // ============================================================ generic (VALU)
 template <int GEN_MAXI>  // c <= 64 * GEN_MAXI
-__global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
+__global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a, Rope rt) {
   extern __shared__ float sq_all[];
   const int row = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
     __builtin_amdgcn_wave_barrier();
     for (int u = lane; u < d_r / 2; u += 64) {
       float cs, sn;
-      rope_cs((double)ctx.qp, u, d_r, a.rope_theta, &cs, &sn);
+      rope_cs(rt, (double)ctx.qp, u, &cs, &sn);
       const int i0 = c - d_r + 2 * u;
       const float x0 = sq[i0], x1 = sq[i0 + 1];
       sq[i0] = x0 * cs - x1 * sn;
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
       if (j < c && j >= c - d_r) {
         const int u = (j - (c - d_r)) >> 1;
         float cs, sn;
-        rope_cs(-(double)ctx.qp, u, d_r, a.rope_theta, &cs, &sn);
+        rope_cs(rt, -(double)ctx.qp, u, &cs, &sn);
         val = (j & 1) ? other * sn + val * cs : val * cs - other * sn;
       }
       if (j < c) {
@@ -161,13 +161,40 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
 // ============================================================ MFMA (c = 512)
 constexpr int AT_C = 512;
 constexpr int AT_TILE = 32;
-constexpr int AT_LDX = AT_C + 8;  // bf16 per LDS row; 16-byte pad
+constexpr int AT_LDX = AT_C + 8;  // bf16 per row of the row-major tile (16-byte pad)
+constexpr int AT_TAB = 2048;      // slots one block can walk
 
-template <int KVF, int NW>
+// Row id of slot v: kv row b*Nmax + s (>= 0), window row -(2 + b*win_len + p % win_len),
+// or -1 for an empty slot.
+__device__ __forceinline__ int slot_row_id(const SlotCtx& x, int v) {
+  if (v < x.kslots) {
+    int s = v;
+    if (x.sparse) {
+      s = x.idx_row[v];
+      if (s < 0 || s >= x.nmax) return -1;
+    } else if (v >= x.nv) {
+      return -1;
+    }
+    return (int)(x.kv_base + s);
+  }
+  const int pw = x.qp - x.n_win + 1 + (v - x.kslots);
+  if (pw < 0 || v - x.kslots >= x.n_win) return -1;
+  return -2 - (int)(x.win_base + pw % x.win_len);
+}
+
+// Physical LDS row of tile entry e.  With 520-element rows this permutation
+// makes both access patterns below free of bank conflicts (32 banks): the
+// 16-byte S^T operand reads (lane li reads entry 8(li/4) + 4nt + li%4) and the
+// 8-byte transpose reads of the P.V operand (16-lane group g reads entries
+// 8g + 4h + q/4).
+__device__ __forceinline__ int xrow(int e) { return (e & 16) | ((e & 7) << 1) | ((e >> 3) & 1); }
+
 struct AttendSmem {
-  uint16_t X[2][AT_TILE][AT_LDX];
-  uint16_t P[NW][16][AT_TILE + 8];
-  int valid[2][AT_TILE];
+  uint16_t Q[64][AT_LDX];           // normalised, RoPE'd queries of the block's 64 heads
+  uint16_t X[2][AT_TILE][AT_LDX];   // gathered rows (double-buffered tiles), rows permuted by xrow
+  int32_t slot[AT_TAB + 64];
+  uint32_t vmask[AT_TAB / 32 + 2];
+  float rcs[AT_C / 2][2];           // cos / sin of the query position for each RoPE pair
 };
 
 // load 8 consecutive elements (dims d..d+7) of a q row as fp32
@@ -187,35 +214,265 @@ __device__ __forceinline__ void load8(const uint8_t* qrow, csa_dtype t, int d, f
   }
 }
 
-template <int KVF, int NW>
-__global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendArgs a, int chunk,
-                                                             int nsplit, float* __restrict__ ws) {
-  __shared__ __attribute__((aligned(16))) AttendSmem<KVF, NW> sm;
-  // block -> (query row, head group of 16*NW heads, slot split)
-  const int hgroups = a.nh / (16 * NW);
+// 8 e4m3 codes (two dwords, element order by byte) -> 8 bf16 (exact)
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = q < 2 ? lo : hi;
+    const int sh = (q & 1) * 16;
+    const float f0 = e4m3_to_f32((w >> sh) & 0xFFu), f1 = e4m3_to_f32((w >> (sh + 8)) & 0xFFu);
+    r[q] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+  }
+  return r;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 4 bf16 of a tile column: transpose read (gfx950 ds_read_b64_tr_b16).  Within a
+// 16-lane group, lane i receives element i%4 of the 8-byte chunks addressed by
+// lanes i/4 + 4j (j = 0..3).
+__device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// One block = one query row x 64 heads x one slot split, 8 waves:
+//  * waves 0-3 (math): wave w owns heads 16w..16w+15 and per 32-slot tile runs
+//      S^T[e][h] = X[e] . q_h       v_mfma_f32_16x16x32_bf16, A = rows, B = q (LDS)
+//      online softmax over e per head (fp32)
+//      O^T[d][h] += sum_e X[e][d] P^T[e][h]   A = rows read transposed, B = P^T
+//    The rows feeding S^T are permuted (lane li reads entry 8(li/4) + 4nt + li%4)
+//    so that each lane's S^T results are exactly the P^T operand it needs
+//    (entries 8g..8g+7 of head li): nothing moves between the two contractions.
+//  * waves 4-7 (loaders): wave 4+w gathers rows 8w..8w+7 of every tile two
+//    tiles ahead into registers (expanding e4m3 to bf16) and commits them to
+//    the LDS tile the math waves are not using.
+// One barrier per tile separates the two buffers.
+template <int KVF>
+__global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt, int chunk,
+                                                         int nsplit, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) AttendSmem sm;
+  const int hgroups = a.nh / 64;
   const int split = blockIdx.x % nsplit;
   const int hg = (blockIdx.x / nsplit) % hgroups;
   const int row = blockIdx.x / (nsplit * hgroups);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool math = wave < 4;
+  const int mw = wave & 3;  // math: head group of the wave; loader: its rows 8mw..8mw+7
   const int g = lane >> 4, li = lane & 15;
-  const int hbase = 16 * NW * hg + 16 * wave;  // first head of this wave
+  const int head = 64 * hg + 16 * mw + li;  // the head of this lane's softmax state (math)
   const int d_r = a.rope_dims;
   const SlotCtx ctx = make_ctx(a, row);
   const int total = ctx.kslots + a.n_win;
   const int v0 = split * chunk;
   const int v1 = min(v0 + chunk, total);
   const int ntiles = v1 > v0 ? (v1 - v0 + AT_TILE - 1) / AT_TILE : 0;
+  const int64_t rb = ctx.rb;
 
-  // ---- query fragments: head 16*wave + li, physical dims 128*g + 8*ks + 0..7
-  bf16x8 qf[16];
+  // ---- raw query row (math waves; the loads overlap the table pass):
+  // head `head`, physical dims 128g + 8ks + 0..7 (the K order of S^T)
+  const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)row * a.nh + head) * row_bytes(a.q_t, AT_C, 0);
+  u32x4 qraw[16];
+  if (math && a.q_t == CSA_BF16) {
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 2 * (128 * g + 8 * ks));
+  }
+
+  // ---- RoPE angles of the query position, one pair per thread (shared by all
+  // heads; the output's inverse rotation reuses them with the sine negated)
+  for (int u = tid; u < d_r / 2; u += 512) {
+    float cs, sn;
+    rope_cs(rt, (double)ctx.qp, u, &cs, &sn);
+    sm.rcs[u][0] = cs;
+    sm.rcs[u][1] = sn;
+  }
+  // ---- slot table and per-tile validity masks (one coalesced pass)
+  for (int i = tid; i < ((ntiles * AT_TILE + 63) & ~63); i += 512) {
+    const int v = v0 + i;
+    const int id = (i < ntiles * AT_TILE && v < v1) ? slot_row_id(ctx, v) : -1;
+    sm.slot[i] = id;
+    const uint64_t bal = __ballot(id != -1);
+    if (lane == 0) {
+      sm.vmask[i >> 5] = (uint32_t)bal;
+      sm.vmask[(i >> 5) + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  __syncthreads();  // slot table and RoPE angles ready
+
+  // ---- loader staging: rows 8mw..8mw+7 of a tile, lane l holds dims 8l..8l+7;
+  // all addresses first (empty slots read row 0 and are zeroed at commit)
+  u32x4 stgA[8], stgB[8];
+  uint32_t okA = 0u, okB = 0u;
+#define CSA_STAGE(STG, OK, T)                                                                \
+  if ((T) < ntiles) {                                                                        \
+    const uint8_t* src[8];                                                                   \
+    OK = 0u;                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
+      const int id = sm.slot[(T) * AT_TILE + 8 * mw + i];                                    \
+      OK |= (id != -1 ? 1u : 0u) << i;                                                       \
+      src[i] = id >= 0 ? ctx.kv + (int64_t)id * rb                                           \
+                       : (id == -1 ? ctx.kv : ctx.win + (int64_t)(-2 - id) * rb);            \
+    }                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
+      if (KVF == CSA_BF16) {                                                                 \
+        STG[i] = *reinterpret_cast<const u32x4*>(src[i] + 16 * lane);                        \
+      } else if (lane < 56) {                                                                \
+        const uint2 w2 = *reinterpret_cast<const uint2*>(src[i] + 8 * lane);                 \
+        STG[i] = u32x4{w2.x, w2.y, 0u, 0u};                                                  \
+      } else {                                                                               \
+        STG[i] = *reinterpret_cast<const u32x4*>(src[i] + 448 + 16 * (lane - 56));           \
+      }                                                                                      \
+    }                                                                                        \
+  }
+#define CSA_COMMIT(STG, OK, BUF)                                                             \
+  {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
+      if (KVF == CSA_FP8MIX && lane < 56) STG[i] = e4m3x8_to_bf16(STG[i][0], STG[i][1]);     \
+      if (!((OK >> i) & 1u)) STG[i] = u32x4{0u, 0u, 0u, 0u};                                 \
+      *reinterpret_cast<u32x4*>(&sm.X[BUF][xrow(8 * mw + i)][8 * lane]) = STG[i];           \
+    }                                                                                        \
+  }
+
+  // transpose-read addresses: lane (g, q = li) reads entry 8g + 4h + li/4,
+  // dims 16nd + 4(li%4) .. +3
+  const int tr_r0 = xrow(8 * g + (li >> 2)), tr_r1 = xrow(8 * g + 4 + (li >> 2));
+  const int tr_c = 4 * (li & 3);
+
+  // one tile on the math waves: S^T, online softmax, O^T (reads X[BUF])
+#define CSA_TILE(T, BUF)                                                                     \
+  {                                                                                          \
+    const uint32_t mask = sm.vmask[T];                                                       \
+    if (mask != 0u) {                                                                        \
+      f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};                    \
+      {                                                                                      \
+        const uint16_t* xr0 = &sm.X[BUF][xrow(8 * (li >> 2) + (li & 3))][128 * g];          \
+        const uint16_t* xr1 = &sm.X[BUF][xrow(8 * (li >> 2) + 4 + (li & 3))][128 * g];      \
+        const uint16_t* qr = &sm.Q[16 * mw + li][128 * g];                                   \
+        u32x4 ra[4], rb4[4], rq[4];                                                          \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                      \
+          ra[q] = *reinterpret_cast<const u32x4*>(xr0 + 8 * q);                              \
+          rb4[q] = *reinterpret_cast<const u32x4*>(xr1 + 8 * q);                             \
+          rq[q] = *reinterpret_cast<const u32x4*>(qr + 8 * q);                               \
+        }                                                                                    \
+        _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                  \
+          const u32x4 a0 = ra[ks & 3], a1 = rb4[ks & 3], bq = rq[ks & 3];                    \
+          if (ks + 4 < 16) {                                                                 \
+            ra[ks & 3] = *reinterpret_cast<const u32x4*>(xr0 + 8 * (ks + 4));                \
+            rb4[ks & 3] = *reinterpret_cast<const u32x4*>(xr1 + 8 * (ks + 4));               \
+            rq[ks & 3] = *reinterpret_cast<const u32x4*>(qr + 8 * (ks + 4));                 \
+          }                                                                                  \
+          const bf16x8 qb = __builtin_bit_cast(bf16x8, bq);                                  \
+          S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb, S[0], 0, 0, 0); \
+          S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb, S[1], 0, 0, 0); \
+        }                                                                                    \
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 1);                                  \
+        _Pragma("unroll") for (int ks = 0; ks < 12; ++ks) {                                  \
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);                                 \
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);                                 \
+        }                                                                                    \
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);                                   \
+      }                                                                                      \
+      float lg[8];                                                                           \
+      float mx = -INFINITY;                                                                  \
+      _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                       \
+      _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                        \
+        const int e = 8 * g + 4 * nt + r;                                                    \
+        const float l = ((mask >> e) & 1u) ? a.scale * S[nt][r] : -INFINITY;                 \
+        lg[4 * nt + r] = l;                                                                  \
+        mx = fmaxf(mx, l);                                                                   \
+      }                                                                                      \
+      mx = fmaxf(mx, __shfl_xor(mx, 16));                                                    \
+      mx = fmaxf(mx, __shfl_xor(mx, 32));                                                    \
+      /* lazy rescale: the reference maximum moves only when a logit exceeds it */          \
+      /* by more than 8 (weights stay below e^8: safe in fp32 sums and bf16 P) */           \
+      const bool grow = mx > m_run + 8.0f;                                                   \
+      if (__any(grow)) {                                                                     \
+        const float m_new = grow ? mx : m_run;                                               \
+        const float alpha = __expf(m_run - m_new);                                           \
+        l_run *= alpha;                                                                      \
+        m_run = m_new;                                                                       \
+        _Pragma("unroll") for (int nd = 0; nd < 32; ++nd) O[nd] *= alpha;                    \
+      }                                                                                      \
+      float pv[8], ps = 0.f;                                                                 \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
+        pv[i] = __expf(lg[i] - m_run);                                                       \
+        ps += pv[i];                                                                         \
+      }                                                                                      \
+      l_run += ps;                                                                           \
+      u32x4 pk;                                                                              \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]); \
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pk); /* P^T: entries 8g..8g+7 of head li */ \
+      {                                                                                      \
+        /* O^T += X^T P^T, operands by transpose reads, 8 column blocks ahead */            \
+        const uint16_t* c0 = &sm.X[BUF][tr_r0][tr_c];                                        \
+        const uint16_t* c1 = &sm.X[BUF][tr_r1][tr_c];                                        \
+        uint2 rx[8][2];                                                                      \
+        _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                      \
+          rx[q][0] = tr_read(c0 + 16 * q);                                                   \
+          rx[q][1] = tr_read(c1 + 16 * q);                                                   \
+        }                                                                                    \
+        _Pragma("unroll") for (int nd = 0; nd < 32; ++nd) {                                  \
+          const u32x4 xa = u32x4{rx[nd & 7][0].x, rx[nd & 7][0].y, rx[nd & 7][1].x, rx[nd & 7][1].y}; \
+          if (nd + 8 < 32) {                                                                 \
+            rx[nd & 7][0] = tr_read(c0 + 16 * (nd + 8));                                     \
+            rx[nd & 7][1] = tr_read(c1 + 16 * (nd + 8));                                     \
+          }                                                                                  \
+          O[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa), pf, O[nd], 0, 0, 0); \
+        }                                                                                    \
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 2);                                  \
+        _Pragma("unroll") for (int nd = 0; nd < 24; ++nd) {                                  \
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                 \
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);                                 \
+        }                                                                                    \
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 2);                                   \
+      }                                                                                      \
+    }                                                                                        \
+  }
+
+  if (!math) {
+    // ---- loaders: tile t+1 is committed into X[(t+1) & 1] while the math
+    // waves read X[t & 1]; set A carries the odd tiles, set B the even ones.
+    // The barrier count matches the math waves': one, then one per tile.
+    CSA_STAGE(stgA, okA, 0);
+    if (ntiles > 0) CSA_COMMIT(stgA, okA, 0);
+    CSA_STAGE(stgA, okA, 1);
+    CSA_STAGE(stgB, okB, 2);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      if (t + 1 < ntiles) {
+        CSA_COMMIT(stgA, okA, 1);
+        CSA_STAGE(stgA, okA, t + 3);
+      }
+      __syncthreads();
+      if (t + 1 >= ntiles) break;
+      if (t + 2 < ntiles) {
+        CSA_COMMIT(stgB, okB, 0);
+        CSA_STAGE(stgB, okB, t + 4);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  float m_run = kNegBig, l_run = 0.f;
+  f32x4 O[32];
   {
-    const int head = hbase + li;
-    const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)row * a.nh + head) * row_bytes(a.q_t, AT_C, 0);
+    // ---- queries to LDS (B operand of S^T): RMSNorm over the head, RoPE at q
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       float v[8];
-      load8(qrow, a.q_t, 128 * g + 8 * ks, v);
+      if (a.q_t == CSA_BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
+          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
+        }
+      } else {
+        load8(qrow, a.q_t, 128 * g + 8 * ks, v);
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
     }
@@ -226,254 +483,143 @@ __global__ __launch_bounds__(NW * 64) void attend_mfma_kernel(AttendArgs a, int 
     for (int ks = 0; ks < 16; ++ks) {
       const int d0 = 128 * g + 8 * ks;
       float v[8];
-      load8(qrow, a.q_t, d0, v);
+      if (a.q_t == CSA_BF16) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] *= inv * (a.q_norm_w ? a.q_norm_w[d0 + j] : 1.f);
-      if (d0 + 8 > AT_C - d_r) {
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
+          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
+        }
+      } else {
+        load8(qrow, a.q_t, d0, v);
+      }
+      if (a.q_norm_w != nullptr) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0 + 4);
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const int d = d0 + j;
-          if (d >= AT_C - d_r) {
-            float cs, sn;
-            rope_cs((double)ctx.qp, (d - (AT_C - d_r)) >> 1, d_r, a.rope_theta, &cs, &sn);
-            const float x0 = v[j], x1 = v[j + 1];
-            v[j] = x0 * cs - x1 * sn;
-            v[j + 1] = x0 * sn + x1 * cs;
-          }
+        for (int j = 0; j < 4; ++j) {
+          v[j] *= inv * g0[j];
+          v[4 + j] *= inv * g1[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] *= inv;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const int d = d0 + j;
+        if (d >= AT_C - d_r) {
+          const float cs = sm.rcs[(d - (AT_C - d_r)) >> 1][0];
+          const float sn = sm.rcs[(d - (AT_C - d_r)) >> 1][1];
+          const float x0 = v[j], x1 = v[j + 1];
+          v[j] = x0 * cs - x1 * sn;
+          v[j + 1] = x0 * sn + x1 * cs;
         }
       }
       u32x4 pk;
 #pragma unroll
       for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-      qf[ks] = __builtin_bit_cast(bf16x8, pk);
+      *reinterpret_cast<u32x4*>(&sm.Q[16 * mw + li][d0]) = pk;
     }
+#pragma unroll
+    for (int nd = 0; nd < 32; ++nd) O[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  // ---- tile staging: each wave gathers rows wave, wave+NW, ... of a tile
-  constexpr int RPW = AT_TILE / NW;
-  u32x4 stg[RPW];
-  int stg_ok[RPW];
-  auto stage = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int rr = wave + NW * i;
-      const int v = v0 + t * AT_TILE + rr;
-      const uint8_t* src = (v < v1) ? ctx.row(v) : nullptr;
-      stg_ok[i] = src != nullptr;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (src != nullptr) {
-        if (KVF == CSA_BF16) {
-          val = *reinterpret_cast<const u32x4*>(src + 16 * lane);
-        } else {  // FP8MIX: 448 e4m3 bytes (lanes 0..27) then 64 bf16 (lanes 28..35)
-          if (lane < 36) val = *reinterpret_cast<const u32x4*>(src + 16 * lane);
-        }
-      }
-      stg[i] = val;
-    }
-  };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int rr = wave + NW * i;
-      uint16_t* dst = &sm.X[buf][rr][0];
-      if (KVF == CSA_BF16) {
-        *reinterpret_cast<u32x4*>(dst + 8 * lane) = stg[i];
-      } else {
-        if (lane < 28) {  // 16 e4m3 -> 16 bf16 (exact)
-          u32x4 lo, hi;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t wv = stg[i][q];
-            const float f0 = e4m3_to_f32(wv & 0xFFu), f1 = e4m3_to_f32((wv >> 8) & 0xFFu);
-            const float f2 = e4m3_to_f32((wv >> 16) & 0xFFu), f3 = e4m3_to_f32(wv >> 24);
-            const uint32_t p0 = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-            const uint32_t p1 = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
-            if (q < 2) { lo[2 * q] = p0; lo[2 * q + 1] = p1; }
-            else { hi[2 * q - 4] = p0; hi[2 * q - 3] = p1; }
-          }
-          *reinterpret_cast<u32x4*>(dst + 16 * lane) = lo;
-          *reinterpret_cast<u32x4*>(dst + 16 * lane + 8) = hi;
-        } else if (lane < 36) {
-          *reinterpret_cast<u32x4*>(dst + 448 + 8 * (lane - 28)) = stg[i];
-        }
-      }
-      if (lane == 0) sm.valid[buf][rr] = stg_ok[i];
-    }
-  };
-
-  float m_run[4], l_run[4];
-  f32x4 O[32];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) { m_run[r] = kNegBig; l_run[r] = 0.f; }
-#pragma unroll
-  for (int nd = 0; nd < 32; ++nd) O[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (ntiles > 0) {
-    stage(0);
-    commit(0);
-  }
-  __syncthreads();
+  __syncthreads();  // queries and tile 0 in LDS
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) stage(t + 1);
-    int any = 0;
-#pragma unroll
-    for (int e = 0; e < AT_TILE; ++e) any |= sm.valid[buf][e];
-    if (any) {
-      // S = Q K^T : two 16-entry sub-tiles, K = 512 in 16 steps
-      f32x4 S[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        S[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t* xr = &sm.X[buf][16 * nt + li][128 * g];
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-          const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xr + 8 * ks));
-          S[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], kb, S[nt], 0, 0, 0);
-        }
-      }
-      // online softmax; lane holds heads 4g+r for entries 16nt+li
-      const int ok0 = sm.valid[buf][li], ok1 = sm.valid[buf][16 + li];
-      float p0[4], p1[4], alpha[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float l0 = ok0 ? a.scale * S[0][r] : -INFINITY;
-        const float l1 = ok1 ? a.scale * S[1][r] : -INFINITY;
-        float mx = fmaxf(l0, l1);
-        mx = fmaxf(mx, __shfl_xor(mx, 1));
-        mx = fmaxf(mx, __shfl_xor(mx, 2));
-        mx = fmaxf(mx, __shfl_xor(mx, 4));
-        mx = fmaxf(mx, __shfl_xor(mx, 8));
-        const float m_new = fmaxf(m_run[r], mx);
-        alpha[r] = __expf(m_run[r] - m_new);
-        p0[r] = __expf(l0 - m_new);
-        p1[r] = __expf(l1 - m_new);
-        l_run[r] = l_run[r] * alpha[r] + p0[r] + p1[r];
-        m_run[r] = m_new;
-      }
-#pragma unroll
-      for (int nd = 0; nd < 32; ++nd)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) O[nd][r] *= alpha[r];
-      // P (bf16) through LDS into the A-operand layout: head li, entries 8g..8g+7
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sm.P[wave][4 * g + r][li] = (uint16_t)f32_to_bf16(p0[r]);
-        sm.P[wave][4 * g + r][16 + li] = (uint16_t)f32_to_bf16(p1[r]);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sm.P[wave][li][8 * g]));
-      // O += P V : V^T fragment = dim 16nd+li, entries 8g..8g+7 (column reads)
-#pragma unroll
-      for (int nd = 0; nd < 32; ++nd) {
-        const uint16_t* xc = &sm.X[buf][8 * g][16 * nd + li];
-        u32x4 vb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vb[i] = (uint32_t)xc[(2 * i) * AT_LDX] | ((uint32_t)xc[(2 * i + 1) * AT_LDX] << 16);
-        O[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, __builtin_bit_cast(bf16x8, vb), O[nd], 0, 0, 0);
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-    if (t + 1 < ntiles) commit(buf ^ 1);
+    CSA_TILE(t, t & 1);
     __syncthreads();
   }
+#undef CSA_TILE
+#undef CSA_STAGE
+#undef CSA_COMMIT
 
-  // ---- per-head totals over the 16 lanes of a row group
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float l = l_run[r];
-    l += __shfl_xor(l, 1);
-    l += __shfl_xor(l, 2);
-    l += __shfl_xor(l, 4);
-    l += __shfl_xor(l, 8);
-    l_run[r] = l;
-  }
+  // ---- lane holds O^T[dim 16nd + 4g + r][head]; head totals across the 4 groups
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16);
+  l_tot += __shfl_xor(l_tot, 32);
   if (nsplit == 1) {
-    // finish: sink in the denominator, normalise, inverse RoPE, store
+    const float z = a.sink[head];
+    const float M = fmaxf(m_run, z);
+    const float em = __expf(m_run - M);
+    const float f = em / (l_tot * em + __expf(z - M));
+    uint8_t* orow = (uint8_t*)a.out + ((int64_t)row * a.nh + head) * row_bytes(a.out_t, AT_C, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int head = hbase + 4 * g + r;
-      const float z = a.sink[head];
-      const float M = fmaxf(m_run[r], z);
-      const float em = __expf(m_run[r] - M);
-      const float f = em / (l_run[r] * em + __expf(z - M));
-      uint8_t* orow = (uint8_t*)a.out + ((int64_t)row * a.nh + head) * row_bytes(a.out_t, AT_C, 0);
+    for (int nd = 0; nd < 32; ++nd) {
+      const int d0 = 16 * nd + 4 * g;
+      float v[4];
 #pragma unroll
-      for (int nd = 0; nd < 32; ++nd) {
-        const int d = 16 * nd + li;
-        float val = O[nd][r] * f;
-        if (16 * nd + 16 > AT_C - d_r) {
-          const float other = __shfl_xor(val, 1);
-          if (d >= AT_C - d_r) {
-            float cs, sn;
-            rope_cs(-(double)ctx.qp, (d - (AT_C - d_r)) >> 1, d_r, a.rope_theta, &cs, &sn);
-            val = (d & 1) ? other * sn + val * cs : val * cs - other * sn;
+      for (int r = 0; r < 4; ++r) v[r] = O[nd][r] * f;
+      if (16 * nd + 16 > AT_C - d_r) {
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          if (d0 + r >= AT_C - d_r) {
+            const float cs = sm.rcs[(d0 + r - (AT_C - d_r)) >> 1][0];
+            const float sn = -sm.rcs[(d0 + r - (AT_C - d_r)) >> 1][1];
+            const float x0 = v[r], x1 = v[r + 1];
+            v[r] = x0 * cs - x1 * sn;
+            v[r + 1] = x0 * sn + x1 * cs;
           }
         }
-        if (a.out_t == CSA_F32) reinterpret_cast<float*>(orow)[d] = val;
-        else reinterpret_cast<uint16_t*>(orow)[d] = (uint16_t)f32_to_bf16(val);
+      }
+      if (a.out_t == CSA_F32) {
+        *reinterpret_cast<f32x4*>(orow + 4 * d0) = f32x4{v[0], v[1], v[2], v[3]};
+      } else {
+        *reinterpret_cast<uint2*>(orow + 2 * d0) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
   } else {
     // partials: O [rows, nsplit, nh, 512] then (m, l) [rows, nsplit, nh, 2]
     const int64_t rs = (int64_t)row * nsplit + split;
-    float* wo = ws + rs * a.nh * AT_C;
-    const int64_t nrows = (int64_t)a.B * a.Tq;
-    float* wml = ws + nrows * nsplit * a.nh * AT_C + rs * a.nh * 2;
+    float* wo = ws + (rs * a.nh + head) * AT_C;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int head = hbase + 4 * g + r;
-#pragma unroll
-      for (int nd = 0; nd < 32; ++nd) wo[(int64_t)head * AT_C + 16 * nd + li] = O[nd][r];
-      if (li == 0) {
-        wml[2 * head] = m_run[r];
-        wml[2 * head + 1] = l_run[r];
-      }
+    for (int nd = 0; nd < 32; ++nd) *reinterpret_cast<f32x4*>(wo + 16 * nd + 4 * g) = O[nd];
+    if (g == 0) {
+      const int64_t nrows = (int64_t)a.B * a.Tq;
+      float* wml = ws + nrows * nsplit * a.nh * AT_C + (rs * a.nh + head) * 2;
+      wml[0] = m_run;
+      wml[1] = l_tot;
     }
   }
 }
 
-// merge split partials in split order, add the sink, normalise, inverse RoPE
-__global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, int nsplit,
+// merge split partials in split order, add the sink, normalise, inverse RoPE;
+// one block per (query row, head), one thread per channel pair
+__global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, Rope rt,
+                                                             int nsplit,
                                                              const float* __restrict__ ws) {
-  const int row = blockIdx.x;
-  const int c = a.c, d_r = a.rope_dims, nh = a.nh;
-  const int qp = a.q_pos[row];
+  const int nh = a.nh, c = a.c, d_r = a.rope_dims;
+  const int row = blockIdx.x / nh, h = blockIdx.x % nh;
+  const int d = 2 * threadIdx.x;
+  if (d >= c) return;
+  const int64_t nrows = (int64_t)a.B * a.Tq;
+  const float* wml = ws + nrows * nsplit * nh * c + (int64_t)row * nsplit * nh * 2;
   const float* wo = ws + (int64_t)row * nsplit * nh * c;
-  const float* wml = ws + (int64_t)gridDim.x * nsplit * nh * c + (int64_t)row * nsplit * nh * 2;
-  const int pairs = c / 2;
-  for (int it = threadIdx.x; it < nh * pairs; it += blockDim.x) {
-    const int h = it / pairs, d = 2 * (it % pairs);
-    const float z = a.sink[h];
-    float M = z;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wml[((int64_t)s * nh + h) * 2]);
-    float den = __expf(z - M), o0 = 0.f, o1 = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float e = __expf(wml[((int64_t)s * nh + h) * 2] - M);
-      den = fmaf(wml[((int64_t)s * nh + h) * 2 + 1], e, den);
-      const float* op = wo + ((int64_t)s * nh + h) * c + d;
-      o0 = fmaf(op[0], e, o0);
-      o1 = fmaf(op[1], e, o1);
-    }
-    o0 /= den;
-    o1 /= den;
-    if (d >= c - d_r) {
-      float cs, sn;
-      rope_cs(-(double)qp, (d - (c - d_r)) >> 1, d_r, a.rope_theta, &cs, &sn);
-      const float x0 = o0, x1 = o1;
-      o0 = x0 * cs - x1 * sn;
-      o1 = x0 * sn + x1 * cs;
-    }
-    const int64_t ob = ((int64_t)row * nh + h) * c + d;
-    if (a.out_t == CSA_F32) {
-      reinterpret_cast<float*>(a.out)[ob] = o0;
-      reinterpret_cast<float*>(a.out)[ob + 1] = o1;
-    } else {
-      reinterpret_cast<uint32_t*>(a.out)[ob / 2] = pack_bf16x2(o0, o1);
-    }
+  const float z = a.sink[h];
+  float M = z;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wml[((int64_t)s * nh + h) * 2]);
+  float den = __expf(z - M), o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float e = __expf(wml[((int64_t)s * nh + h) * 2] - M);
+    den = fmaf(wml[((int64_t)s * nh + h) * 2 + 1], e, den);
+    const float2 v = *reinterpret_cast<const float2*>(wo + ((int64_t)s * nh + h) * c + d);
+    o0 = fmaf(v.x, e, o0);
+    o1 = fmaf(v.y, e, o1);
+  }
+  const float inv = 1.0f / den;
+  o0 *= inv;
+  o1 *= inv;
+  if (d >= c - d_r) {
+    float cs, sn;
+    rope_cs(rt, -(double)a.q_pos[row], (d - (c - d_r)) >> 1, &cs, &sn);
+    const float x0 = o0, x1 = o1;
+    o0 = x0 * cs - x1 * sn;
+    o1 = x0 * sn + x1 * cs;
+  }
+  const int64_t ob = ((int64_t)row * nh + h) * c + d;
+  if (a.out_t == CSA_F32) {
+    reinterpret_cast<float2*>(a.out)[ob / 2] = make_float2(o0, o1);
+  } else {
+    reinterpret_cast<uint32_t*>(a.out)[ob / 2] = pack_bf16x2(o0, o1);
   }
 }
 
@@ -489,13 +635,13 @@ static bool use_mfma(const AttendArgs& a) {
 static void plan_splits(const AttendArgs& a, int* chunk, int* nsplit) {
   const int kslots = a.idx ? a.k : a.Nmax;
   const int total = kslots + a.n_win;
-  if (a.Tq > 1 || total <= 256) {
+  if ((a.Tq > 1 || total <= 256) && total <= AT_TAB) {
     *chunk = ((total + AT_TILE - 1) / AT_TILE) * AT_TILE;
     *nsplit = 1;
     return;
   }
-  int ch = ((total / 16 + AT_TILE - 1) / AT_TILE) * AT_TILE;
-  ch = ch < 128 ? 128 : (ch > 1024 ? 1024 : ch);
+  int ch = ((total / 8 + AT_TILE - 1) / AT_TILE) * AT_TILE;
+  ch = ch < 128 ? 128 : (ch > AT_TAB ? AT_TAB : ch);
   *chunk = ch;
   *nsplit = (total + ch - 1) / ch;
 }
@@ -512,30 +658,31 @@ size_t attend_workspace(const AttendArgs& a) {
 hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s) {
   const int rows = a.B * a.Tq;
   if (rows == 0) return hipSuccess;
+  const Rope rt = make_rope(a.rope_dims, a.rope_theta);
   if (!use_mfma(a)) {
     const int nw = a.nh < 4 ? a.nh : 4;
     const size_t shm = (size_t)nw * a.c * sizeof(float);
     if (a.c <= 64)
-      hipLaunchKernelGGL(attend_generic_kernel<1>, dim3(rows), dim3(64 * nw), shm, s, a);
+      hipLaunchKernelGGL(attend_generic_kernel<1>, dim3(rows), dim3(64 * nw), shm, s, a, rt);
     else if (a.c <= 128)
-      hipLaunchKernelGGL(attend_generic_kernel<2>, dim3(rows), dim3(64 * nw), shm, s, a);
+      hipLaunchKernelGGL(attend_generic_kernel<2>, dim3(rows), dim3(64 * nw), shm, s, a, rt);
     else if (a.c <= 512)
-      hipLaunchKernelGGL(attend_generic_kernel<8>, dim3(rows), dim3(64 * nw), shm, s, a);
+      hipLaunchKernelGGL(attend_generic_kernel<8>, dim3(rows), dim3(64 * nw), shm, s, a, rt);
     else
-      hipLaunchKernelGGL(attend_generic_kernel<16>, dim3(rows), dim3(64 * nw), shm, s, a);
+      hipLaunchKernelGGL(attend_generic_kernel<16>, dim3(rows), dim3(64 * nw), shm, s, a, rt);
     return hipGetLastError();
   }
   int chunk, nsplit;
   plan_splits(a, &chunk, &nsplit);
   dim3 grid((unsigned)((int64_t)nsplit * (a.nh / 64) * rows));
   float* w = (float*)ws;
-#define CSA_LAUNCH(KVF, NW) \
-  hipLaunchKernelGGL((attend_mfma_kernel<KVF, NW>), grid, dim3(NW * 64), 0, s, a, chunk, nsplit, w)
-  if (a.kv_t == CSA_BF16) CSA_LAUNCH(CSA_BF16, 4);
-  else CSA_LAUNCH(CSA_FP8MIX, 4);
-#undef CSA_LAUNCH
+  if (a.kv_t == CSA_BF16)
+    hipLaunchKernelGGL(attend_mfma_kernel<CSA_BF16>, grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+  else
+    hipLaunchKernelGGL(attend_mfma_kernel<CSA_FP8MIX>, grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   if (nsplit > 1)
-    hipLaunchKernelGGL(attend_combine_kernel, dim3(rows), dim3(256), 0, s, a, nsplit, (const float*)w);
+    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((int64_t)rows * a.nh)),
+                       dim3((a.c / 2 + 63) / 64 * 64), 0, s, a, rt, nsplit, (const float*)w);
   return hipGetLastError();
 }
 

@@ -110,15 +110,49 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ------------------------------------------------------------------ RoPE
-// cos/sin of pos * theta^(-2u/d_r), the angle formed and reduced in fp64 so
-// that positions up to 2^31 keep full fp32 accuracy
-__device__ __forceinline__ void rope_cs(double pos, int u, int d_r, float theta,
-                                        float* c, float* s) {
-  const double freq = pow((double)theta, -2.0 * (double)u / (double)d_r);
-  double sd, cd;
-  sincos(pos * freq, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
+// Pair u of d_r RoPE channels turns by pos * f_u, f_u = theta^(-2u/d_r).  The
+// host passes base = theta^(-2/d_r) in fp64; a kernel forms f_u = base^u by
+// binary powering (relative error < 2e-15), the angle pos * f_u in fp64 and
+// reduces it to a quarter turn in fp64, so positions up to 2^31 keep full fp32
+// accuracy.  sin / cos of the remainder |t| <= pi/4 come from their Taylor
+// series (truncation below 3e-9), evaluated in fp32 without branches.
+struct Rope {
+  double base;  // theta^(-2/d_r)
+  int d_r;
+};
+
+inline Rope make_rope(int d_r, float theta) {
+  Rope r;
+  r.d_r = d_r;
+  r.base = d_r > 0 ? pow((double)theta, -2.0 / (double)d_r) : 1.0;
+  return r;
+}
+
+__device__ __forceinline__ double rope_freq(double base, int u) {
+  double f = 1.0, p = base;
+  for (int e = u; e > 0; e >>= 1) {
+    if (e & 1) f *= p;
+    p *= p;
+  }
+  return f;
+}
+
+// sin and cos of an angle given in fp64 radians
+__device__ __forceinline__ void sincos_fp64_angle(double ang, float* s, float* c) {
+  const double q = rint(ang * 0.6366197723675814);        // quarter turns
+  const float t = (float)fma(-q, 1.5707963267948966, ang);  // |t| <= pi/4
+  const float t2 = t * t;
+  const float sp = t * (1.0f + t2 * (-1.0f / 6 + t2 * (1.0f / 120 + t2 * (-1.0f / 5040 + t2 * (1.0f / 362880)))));
+  const float cp = 1.0f + t2 * (-0.5f + t2 * (1.0f / 24 + t2 * (-1.0f / 720 + t2 * (1.0f / 40320 + t2 * (-1.0f / 3628800)))));
+  const int n = (int)((long long)q & 3);
+  const float ss = (n & 1) ? cp : sp;
+  const float cc = (n & 1) ? sp : cp;
+  *s = (n & 2) ? -ss : ss;
+  *c = ((n + 1) & 2) ? -cc : cc;
+}
+
+__device__ __forceinline__ void rope_cs(const Rope& r, double pos, int u, float* c, float* s) {
+  sincos_fp64_angle(pos * rope_freq(r.base, u), s, c);
 }
 
 // ------------------------------------------------------------------ row formats

@@ -17,7 +17,7 @@ namespace csa {
 // =============================================================== row prep
 __global__ __launch_bounds__(256) void prep_rows_kernel(
     const uint8_t* __restrict__ x, csa_dtype x_t, int c, const float* __restrict__ norm_w,
-    float eps, int d_r, float theta, const int32_t* __restrict__ pos, int rows_per_seq,
+    float eps, int d_r, Rope rt, const int32_t* __restrict__ pos, int rows_per_seq,
     int pos_stride, int pos_offset, uint8_t* __restrict__ out, uint8_t* __restrict__ out_scale,
     csa_dtype out_t) {
   extern __shared__ float smem[];
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void prep_rows_kernel(
   const double p = pos != nullptr ? (double)pos[r]
                                   : (double)pos_offset + (double)pos_stride * (double)(r % rows_per_seq);
   const int64_t ob = row_bytes(out_t, c, d_r);
-  finish_row(row, c, norm_w, eps, d_r, theta, p, out + r * ob,
+  finish_row(row, c, norm_w, eps, d_r, rt, p, out + r * ob,
              out_t == CSA_MXFP4 ? out_scale + r * (c / 32) : nullptr, out_t, red);
 }
 
@@ -42,8 +42,9 @@ hipError_t launch_prep_rows(const void* x, csa_dtype x_t, int64_t rows, int c,
   // one 256-thread block per row; rows <= 2^24 keeps the grid within 2^32 lanes
   const size_t shm = (size_t)(c + 16) * sizeof(float);
   hipLaunchKernelGGL(prep_rows_kernel, dim3((unsigned)rows), dim3(256), shm, s,
-                     (const uint8_t*)x, x_t, c, norm_w, eps, rope_dims, rope_theta, pos,
-                     rows_per_seq, pos_stride, pos_offset, (uint8_t*)out, out_scale, out_t);
+                     (const uint8_t*)x, x_t, c, norm_w, eps, rope_dims,
+                     make_rope(rope_dims, rope_theta), pos, rows_per_seq, pos_stride,
+                     pos_offset, (uint8_t*)out, out_scale, out_t);
   return hipGetLastError();
 }
 
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
     const float* __restrict__ Ca, const float* __restrict__ Za, const float* __restrict__ Cb,
     const float* __restrict__ Zb, const float* __restrict__ bias_a,
     const float* __restrict__ bias_b, int T, int m, int c, const float* __restrict__ norm_w,
-    float eps, int d_r, float theta, int pos_stride, int pos_offset, uint8_t* __restrict__ out,
+    float eps, int d_r, Rope rt, int pos_stride, int pos_offset, uint8_t* __restrict__ out,
     uint8_t* __restrict__ out_scale, csa_dtype out_t) {
   extern __shared__ float smem[];
   float* row = smem;
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
   __syncthreads();
   const int64_t r = (int64_t)b * n_out + i;
   const int64_t ob = row_bytes(out_t, c, d_r);
-  finish_row(row, c, norm_w, eps, d_r, theta, (double)pos_stride * i + pos_offset, out + r * ob,
+  finish_row(row, c, norm_w, eps, d_r, rt, (double)pos_stride * i + pos_offset, out + r * ob,
              out_t == CSA_MXFP4 ? out_scale + r * (c / 32) : nullptr, out_t, red);
 }
 
@@ -269,7 +270,8 @@ hipError_t launch_pool(const float* Ca, const float* Za, const float* Cb, const 
   if (n_out == 0 || B == 0) return hipSuccess;
   const size_t shm = (size_t)(c + 16) * sizeof(float);
   hipLaunchKernelGGL(pool_kernel, dim3(n_out, B), dim3(256), shm, s, Ca, Za, Cb, Zb, bias_a,
-                     bias_b, T, m, c, norm_w, eps, rope_dims, rope_theta, pos_stride, pos_offset,
+                     bias_b, T, m, c, norm_w, eps, rope_dims,
+                     make_rope(rope_dims, rope_theta), pos_stride, pos_offset,
                      (uint8_t*)out, out_scale, out_t);
   return hipGetLastError();
 }

@@ -125,25 +125,44 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_mfma_kernel(
     for (int r = 0; r < 16; ++r)
       wr[mt][r] = w[(int64_t)row * 64 + 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3)];
 
-  for (int base = e0 + wave * IDX_SUB; base < e1; base += IDX_WAVES * IDX_SUB) {
+  // raw key bytes of one 32-entry sub-tile (bf16: 128 B per lane; MXFP4: 32 B
+  // of codes + the row's 4 scale bytes), prefetched one sub-tile ahead
+  struct Raw {
+    u32x4 v[MX ? 2 : 8];
+    uint32_t sc;
+  };
+  auto fetch = [&](int base, Raw& r) {
     const int n = base + col;
-    const bool valid = n < e1;
-    const int64_t kr = (int64_t)b * Nmax + (valid ? n : e0);
-    bf16x8 bfr[8];
+    const int64_t kr = (int64_t)b * Nmax + (n < e1 ? n : e0);
     if (!MX) {
       const u32x4* p = reinterpret_cast<const u32x4*>(kI + kr * 256 + 128 * half);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) bfr[ks] = __builtin_bit_cast(bf16x8, p[ks]);
+      for (int ks = 0; ks < 8; ++ks) r.v[ks] = p[ks];
+      r.sc = 0;
     } else {
       const u32x4* p = reinterpret_cast<const u32x4*>(kI + kr * 64 + 32 * half);
-      const u32x4 w0 = p[0], w1 = p[1];
-      const uint32_t sc = *reinterpret_cast<const uint32_t*>(kI_scale + kr * 4);
-      const float s0 = exp2i((int)((sc >> (16 * half)) & 0xFFu) - 127);
-      const float s1 = exp2i((int)((sc >> (16 * half + 8)) & 0xFFu) - 127);
+      r.v[0] = p[0];
+      r.v[1] = p[1];
+      r.sc = *reinterpret_cast<const uint32_t*>(kI_scale + kr * 4);
+    }
+  };
+  constexpr int STEP = IDX_WAVES * IDX_SUB;
+  Raw cur, nxt;
+  int base = e0 + wave * IDX_SUB;
+  if (base < e1) fetch(base, cur);
+  for (; base < e1; base += STEP) {
+    if (base + STEP < e1) fetch(base + STEP, nxt);
+    bf16x8 bfr[8];
+    if (!MX) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bfr[ks] = e2m1x8_to_bf16(w0[ks], s0);
+      for (int ks = 0; ks < 8; ++ks) bfr[ks] = __builtin_bit_cast(bf16x8, cur.v[ks]);
+    } else {
+      const float s0 = exp2i((int)((cur.sc >> (16 * half)) & 0xFFu) - 127);
+      const float s1 = exp2i((int)((cur.sc >> (16 * half + 8)) & 0xFFu) - 127);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bfr[4 + ks] = e2m1x8_to_bf16(w1[ks], s1);
+      for (int ks = 0; ks < 4; ++ks) bfr[ks] = e2m1x8_to_bf16(cur.v[0][ks], s0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bfr[4 + ks] = e2m1x8_to_bf16(cur.v[1][ks], s1);
     }
     f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
@@ -151,20 +170,22 @@ __global__ __launch_bounds__(IDX_WAVES * 64) void indexer_mfma_kernel(
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[0][ks], bfr[ks], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[1][ks], bfr[ks], acc1, 0, 0, 0);
     }
-    float s = 0.f;
+    float sc = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s = fmaf(wr[0][r], fmaxf(acc0[r], 0.f), s);
-      s = fmaf(wr[1][r], fmaxf(acc1[r], 0.f), s);
+      sc = fmaf(wr[0][r], fmaxf(acc0[r], 0.f), sc);
+      sc = fmaf(wr[1][r], fmaxf(acc1[r], 0.f), sc);
     }
-    s += __shfl_xor(s, 32);
-    if (half == 0 && valid) {
+    sc += __shfl_xor(sc, 32);
+    const int n = base + col;
+    if (half == 0 && n < e1) {
       const int64_t o = (int64_t)row * Nmax + n;
       if (score_bf16)
-        reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(s);
+        reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(sc);
       else
-        reinterpret_cast<float*>(scores)[o] = s;
+        reinterpret_cast<float*>(scores)[o] = sc;
     }
+    cur = nxt;
   }
 }
 
@@ -176,7 +197,11 @@ hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_
   if (rows == 0 || Nmax == 0) return hipSuccess;
   const int sbf = score_t == CSA_BF16;
   if ((in_t == CSA_BF16 || in_t == CSA_MXFP4) && nI == 64 && cI == 128) {
-    const int epb = 512;
+    // about three blocks per CU over the whole call; a block covers a
+    // multiple of 128 entries (4 waves x 32)
+    const int64_t want = ((int64_t)Nmax * rows + 767) / 768;
+    int epb = (int)(((want + 127) / 128) * 128);
+    epb = epb < 256 ? 256 : (epb > 8192 ? 8192 : epb);
     dim3 grid((unsigned)(((int64_t)Nmax + epb - 1) / epb * rows));
     if (in_t == CSA_BF16)
       hipLaunchKernelGGL(indexer_mfma_kernel<false>, grid, dim3(IDX_WAVES * 64), 0, s,

@@ -22,7 +22,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // Evidence Ledger Section 2.3.3: RMSNorm of the entry, then RoPE of its last
 // d_r channels (adjacent pairs) at `pos`; then the row is stored in out_t.
 __device__ void finish_row(float* row, int c, const float* __restrict__ norm_w, float eps,
-                           int d_r, float theta, double pos, uint8_t* __restrict__ out,
+                           int d_r, const Rope& rt, double pos, uint8_t* __restrict__ out,
                            uint8_t* __restrict__ out_scale, csa_dtype out_t, float* red) {
   const int tid = threadIdx.x, nt = blockDim.x;
   if (norm_w != nullptr) {
@@ -36,7 +36,7 @@ __device__ void finish_row(float* row, int c, const float* __restrict__ norm_w, 
   if (d_r > 0) {
     for (int u = tid; u < d_r / 2; u += nt) {
       float cs, sn;
-      rope_cs(pos, u, d_r, theta, &cs, &sn);
+      rope_cs(rt, pos, u, &cs, &sn);
       const int i0 = c - d_r + 2 * u;
       const float a = row[i0], b = row[i0 + 1];
       row[i0] = a * cs - b * sn;
