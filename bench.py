@@ -134,6 +134,7 @@ def run_decode(args, torch, I, G):
                 if v is not None:
                     setattr(c, name, v.clone())
             c.ws = None
+            c.ws_topk = None
             copies.append(c)
         for c in copies:                         # workspace sizing outside the timed region
             G.decode_step(c, stream)

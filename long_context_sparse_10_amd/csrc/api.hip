@@ -170,9 +170,10 @@ csa_status topk_select(const void* scores, csa_dtype score_t, const int32_t* q_p
   if ((int64_t)B * Tq > INT_MAX) return CSA_ERR_INVALID;
   if (!is_f32_bf16(score_t)) return CSA_ERR_UNSUPPORTED;
   csa_status st;
-  if (ws_query(ws, ws_bytes, 0, &st)) return st;
+  if (ws_query(ws, ws_bytes, topk_workspace(B, Tq, Nmax), &st)) return st;
   if (B == 0 || Tq == 0) return CSA_OK;
-  return launch_status(launch_topk(scores, score_t, q_pos, n_entries, B, Tq, Nmax, m, k, idx, stream));
+  return launch_status(launch_topk(scores, score_t, q_pos, n_entries, B, Tq, Nmax, m, k, idx, ws,
+                                   stream));
 }
 
 static csa_status attend_common(AttendArgs& a, void* ws, size_t* ws_bytes, hipStream_t stream) {

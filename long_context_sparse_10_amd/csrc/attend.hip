@@ -271,14 +271,15 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   const int ntiles = v1 > v0 ? (v1 - v0 + AT_TILE - 1) / AT_TILE : 0;
   const int64_t rb = ctx.rb;
 
-  // ---- raw query row (math waves; the loads overlap the table pass):
-  // head `head`, physical dims 128g + 8ks + 0..7 (the K order of S^T)
-  const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)row * a.nh + head) * row_bytes(a.q_t, AT_C, 0);
-  u32x4 qraw[16];
-  if (math && a.q_t == CSA_BF16) {
+  // ---- raw query rows, loads issued first so they overlap the table pass:
+  // wave w prepares heads 8w..8w+7 of the block, 8 lanes per head, lane part p
+  // holding dims 64j + 8p .. +7 (j = 0..7)
+  const int qhl = 8 * wave + (lane >> 3), qp8 = 8 * (lane & 7);
+  const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)row * a.nh + 64 * hg + qhl) * row_bytes(a.q_t, AT_C, 0);
+  u32x4 qraw[8];
+  if (a.q_t == CSA_BF16) {
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-      qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 2 * (128 * g + 8 * ks));
+    for (int j = 0; j < 8; ++j) qraw[j] = *reinterpret_cast<const u32x4*>(qrow + 2 * (64 * j + qp8));
   }
 
   // ---- RoPE angles of the query position, one pair per thread (shared by all
@@ -302,10 +303,65 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   }
   __syncthreads();  // slot table and RoPE angles ready
 
+  // ---- queries to LDS (B operand of S^T): RMSNorm over the head, RoPE at q
+#define CSA_QPREP()                                                                          \
+  {                                                                                          \
+    float ss = 0.f;                                                                          \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                          \
+      float v[8];                                                                            \
+      if (a.q_t == CSA_BF16) {                                                               \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+          v[2 * i] = __uint_as_float(qraw[j][i] << 16);                                      \
+          v[2 * i + 1] = __uint_as_float(qraw[j][i] & 0xFFFF0000u);                          \
+        }                                                                                    \
+      } else {                                                                               \
+        load8(qrow, a.q_t, 64 * j + qp8, v);                                                 \
+      }                                                                                      \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);               \
+    }                                                                                        \
+    ss += __shfl_xor(ss, 1);                                                                 \
+    ss += __shfl_xor(ss, 2);                                                                 \
+    ss += __shfl_xor(ss, 4);                                                                 \
+    const float inv = 1.0f / sqrtf(ss / (float)AT_C + a.eps);                                \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                          \
+      const int d0 = 64 * j + qp8;                                                           \
+      float v[8];                                                                            \
+      if (a.q_t == CSA_BF16) {                                                               \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+          v[2 * i] = __uint_as_float(qraw[j][i] << 16);                                      \
+          v[2 * i + 1] = __uint_as_float(qraw[j][i] & 0xFFFF0000u);                          \
+        }                                                                                    \
+      } else {                                                                               \
+        load8(qrow, a.q_t, d0, v);                                                           \
+      }                                                                                      \
+      if (a.q_norm_w != nullptr) {                                                           \
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0);                   \
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0 + 4);               \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+          v[i] *= inv * g0[i];                                                               \
+          v[4 + i] *= inv * g1[i];                                                           \
+        }                                                                                    \
+      } else {                                                                               \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) v[i] *= inv;                           \
+      }                                                                                      \
+      _Pragma("unroll") for (int i = 0; i < 8; i += 2) {                                     \
+        const int d = d0 + i;                                                                \
+        if (d >= AT_C - d_r) {                                                               \
+          const float cs = sm.rcs[(d - (AT_C - d_r)) >> 1][0];                               \
+          const float sn = sm.rcs[(d - (AT_C - d_r)) >> 1][1];                               \
+          const float x0 = v[i], x1 = v[i + 1];                                              \
+          v[i] = x0 * cs - x1 * sn;                                                          \
+          v[i + 1] = x0 * sn + x1 * cs;                                                      \
+        }                                                                                    \
+      }                                                                                      \
+      u32x4 pk;                                                                              \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]); \
+      *reinterpret_cast<u32x4*>(&sm.Q[qhl][d0]) = pk;                                        \
+    }                                                                                        \
+  }
+
   // ---- loader staging: rows 8mw..8mw+7 of a tile, lane l holds dims 8l..8l+7;
   // all addresses first (empty slots read row 0 and are zeroed at commit)
-  u32x4 stgA[8], stgB[8];
-  uint32_t okA = 0u, okB = 0u;
 #define CSA_STAGE(STG, OK, T)                                                                \
   if ((T) < ntiles) {                                                                        \
     const uint8_t* src[8];                                                                   \
@@ -433,96 +489,42 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   }
 
   if (!math) {
-    // ---- loaders: tile t+1 is committed into X[(t+1) & 1] while the math
-    // waves read X[t & 1]; set A carries the odd tiles, set B the even ones.
-    // The barrier count matches the math waves': one, then one per tile.
-    CSA_STAGE(stgA, okA, 0);
-    if (ntiles > 0) CSA_COMMIT(stgA, okA, 0);
-    CSA_STAGE(stgA, okA, 1);
-    CSA_STAGE(stgB, okB, 2);
+    // ---- loaders: a ring of 4 register sets keeps 4 tiles in flight; tile u
+    // lives in set u % 4.  While the math waves compute tile t from X[t & 1],
+    // tile t+1 is committed into X[(t+1) & 1] and tile t+5 is fetched into
+    // the set it frees.  The barrier count matches the math waves': one, then
+    // one per tile.
+    u32x4 st0[8], st1[8], st2[8], st3[8];
+    uint32_t ok0 = 0u, ok1 = 0u, ok2 = 0u, ok3 = 0u;
+    CSA_STAGE(st0, ok0, 0);
+    CSA_STAGE(st1, ok1, 1);
+    CSA_STAGE(st2, ok2, 2);
+    CSA_STAGE(st3, ok3, 3);
+    CSA_QPREP();
+    if (ntiles > 0) CSA_COMMIT(st0, ok0, 0);
+    CSA_STAGE(st0, ok0, 4);
     __syncthreads();
-    for (int t = 0; t < ntiles; t += 2) {
-      if (t + 1 < ntiles) {
-        CSA_COMMIT(stgA, okA, 1);
-        CSA_STAGE(stgA, okA, t + 3);
-      }
-      __syncthreads();
-      if (t + 1 >= ntiles) break;
-      if (t + 2 < ntiles) {
-        CSA_COMMIT(stgB, okB, 0);
-        CSA_STAGE(stgB, okB, t + 4);
-      }
-      __syncthreads();
+#define CSA_PHASE(STG, OK, J)                                                                \
+    if (t + (J) < ntiles) {                                                                  \
+      CSA_COMMIT(STG, OK, (J) & 1);                                                          \
+      CSA_STAGE(STG, OK, t + (J) + 4);                                                       \
+    }                                                                                        \
+    __syncthreads();                                                                         \
+    if (t + (J) >= ntiles) break;
+    for (int t = 0; t < ntiles; t += 4) {
+      CSA_PHASE(st1, ok1, 1);
+      CSA_PHASE(st2, ok2, 2);
+      CSA_PHASE(st3, ok3, 3);
+      CSA_PHASE(st0, ok0, 4);
     }
+#undef CSA_PHASE
     return;
   }
   float m_run = kNegBig, l_run = 0.f;
   f32x4 O[32];
-  {
-    // ---- queries to LDS (B operand of S^T): RMSNorm over the head, RoPE at q
-    float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      float v[8];
-      if (a.q_t == CSA_BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
-          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
-        }
-      } else {
-        load8(qrow, a.q_t, 128 * g + 8 * ks, v);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
-    }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    const float inv = 1.0f / sqrtf(ss / (float)AT_C + a.eps);
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const int d0 = 128 * g + 8 * ks;
-      float v[8];
-      if (a.q_t == CSA_BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
-          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
-        }
-      } else {
-        load8(qrow, a.q_t, d0, v);
-      }
-      if (a.q_norm_w != nullptr) {
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0 + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[j] *= inv * g0[j];
-          v[4 + j] *= inv * g1[j];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] *= inv;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const int d = d0 + j;
-        if (d >= AT_C - d_r) {
-          const float cs = sm.rcs[(d - (AT_C - d_r)) >> 1][0];
-          const float sn = sm.rcs[(d - (AT_C - d_r)) >> 1][1];
-          const float x0 = v[j], x1 = v[j + 1];
-          v[j] = x0 * cs - x1 * sn;
-          v[j + 1] = x0 * sn + x1 * cs;
-        }
-      }
-      u32x4 pk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
-      *reinterpret_cast<u32x4*>(&sm.Q[16 * mw + li][d0]) = pk;
-    }
-#pragma unroll
-    for (int nd = 0; nd < 32; ++nd) O[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int nd = 0; nd < 32; ++nd) O[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  CSA_QPREP();
   __syncthreads();  // queries and tile 0 in LDS
   for (int t = 0; t < ntiles; ++t) {
     CSA_TILE(t, t & 1);
@@ -531,6 +533,7 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
 #undef CSA_TILE
 #undef CSA_STAGE
 #undef CSA_COMMIT
+#undef CSA_QPREP
 
   // ---- lane holds O^T[dim 16nd + 4g + r][head]; head totals across the 4 groups
   float l_tot = l_run;
@@ -596,8 +599,10 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, Rope 
   const float* wo = ws + (int64_t)row * nsplit * nh * c;
   const float z = a.sink[h];
   float M = z;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wml[((int64_t)s * nh + h) * 2]);
   float den = __expf(z - M), o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) {
     const float e = __expf(wml[((int64_t)s * nh + h) * 2] - M);
     den = fmaf(wml[((int64_t)s * nh + h) * 2 + 1], e, den);
@@ -640,8 +645,11 @@ static void plan_splits(const AttendArgs& a, int* chunk, int* nsplit) {
     *nsplit = 1;
     return;
   }
-  int ch = ((total / 8 + AT_TILE - 1) / AT_TILE) * AT_TILE;
-  ch = ch < 128 ? 128 : (ch > AT_TAB ? AT_TAB : ch);
+  // 8 splits up to 4096 slots, 16 beyond: a decode batch of 16-32 rows then
+  // gives one block per compute unit
+  const int want = total <= 4096 ? 8 : 16;
+  int ch = ((total + want - 1) / want + AT_TILE - 1) / AT_TILE * AT_TILE;
+  ch = ch < 4 * AT_TILE ? 4 * AT_TILE : (ch > AT_TAB ? AT_TAB : ch);
   *chunk = ch;
   *nsplit = (total + ch - 1) / ch;
 }

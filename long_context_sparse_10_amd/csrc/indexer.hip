@@ -2,15 +2,15 @@
 //   score(t, s) = sum_h w[t, h] * ReLU(qI[t, h] . kI[s])   for s < N(q_t).
 //
 // Hot shape (cI = 128, nI = 64, bf16 or MXFP4): the q.k contraction runs on
-// v_mfma_f32_32x32x16_bf16 with the 64 heads as the M dimension (two 32-row
-// tiles) and 32 entries per wave as N, K = 128.  Each lane then holds one
-// entry column and 16 head rows of each tile, so the ReLU-weighted head
-// reduction is 32 in-register FMAs plus one exchange with the lane 32 apart.
-// Index keys stream straight from HBM into MFMA operand registers: the K order
-// inside an MFMA is free, so lane half h takes 128 (bf16) or 32 (MXFP4)
-// contiguous bytes of its entry's row and the query fragments use the same
-// permutation.  MXFP4 codes are expanded to bf16 in registers (exact: an E2M1
-// value times a power of two has at most two significant bits).
+// the matrix cores with the 64 heads as the M dimension (four 16-row tiles)
+// and 16 entries per group as N, K = 128.  Each lane then holds one entry
+// column and 4 head rows of each tile, so the ReLU-weighted head reduction is
+// 16 in-register FMAs plus two exchanges across the lane groups.  Index keys
+// stream straight from HBM into MFMA operand registers: the K order inside an
+// MFMA is free, so the lanes of an entry take contiguous bytes of its row and
+// the query fragments use the same permutation.  MXFP4 keys and queries go to the
+// block-scaled fp4 MFMA as stored (E2M1 codes plus e8m0 scales); products of
+// E2M1 values times powers of two are exact and accumulate in fp32.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -64,128 +64,139 @@ __global__ __launch_bounds__(256) void indexer_generic_kernel(
 }
 
 // ------------------------------------------------------------------ MFMA (nI 64, cI 128)
-// 8 packed E2M1 codes (one dword, even element in the low nibble) -> 8 bf16
-__device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t word, float scale) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = e2m1_to_f32((word >> (8 * i)) & 15u) * scale;
-    const float hi = e2m1_to_f32((word >> (8 * i + 4)) & 15u) * scale;
-    r[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);  // exact
-  }
-  return __builtin_bit_cast(bf16x8, r);
+constexpr int IDX_WAVES = 4;
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8 widen(u32x4 v) {
+  return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
 }
 
-constexpr int IDX_WAVES = 4;
-constexpr int IDX_SUB = 32;  // entries per wave sub-tile
-
+// One block = 4 waves over a contiguous entry range of one query row.  The
+// contraction uses 16x16 matrix-core tiles: 4 tiles of 16 heads (M) by 16
+// entries (N).  Lane (col, kg) = (lane % 16, lane / 16) holds entry col; the
+// four lanes of an entry read adjacent 16-byte pieces of its row, so every
+// load instruction covers 16 rows in 64-byte contiguous runs.
+//  * bf16: v_mfma_f32_16x16x32_bf16, step ks covers row bytes 64ks .. 64ks+63
+//    (lane kg: dims 32ks + 8kg .. +7), K = 128 in 4 steps.
+//  * MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4, one instruction per tile: lane
+//    kg holds code bytes 16kg .. 16kg+15 (dims 32kg .. 32kg+31), exactly the
+//    32-element block whose e8m0 scale the matrix core applies.
+// A wave scores G groups of 16 entries per step (bf16 G = 2, MXFP4 G = 8) and
+// keeps a ring of three steps of raw key bytes in registers: two in flight
+// while the third is scored.
 template <bool MX>
-__global__ __launch_bounds__(IDX_WAVES * 64) void indexer_mfma_kernel(
+__global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ kI,
     const uint8_t* __restrict__ kI_scale, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int Nmax, int m, int ent_per_block,
     void* __restrict__ scores, int score_bf16) {
+  constexpr int G = MX ? 8 : 2;
   const int tiles = (Nmax + ent_per_block - 1) / ent_per_block;
   const int row = blockIdx.x / tiles, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, col = lane & 31;
+  const int kg = lane >> 4, col = lane & 15;
   const int nv = min(min(n_entries[b], Nmax), (q_pos[row] + 1) / m);
   const int e0 = (blockIdx.x % tiles) * ent_per_block;
   if (e0 >= nv) return;
   const int e1 = min(e0 + ent_per_block, nv);
 
-  // query fragments: head 32*mt + col, physical dims 64*half + 8*ks + 0..7
-  bf16x8 afr[2][8];
+  // query fragments of head 16*mt + col in the keys' K order
+  bf16x8 afr[4][MX ? 1 : 4];
+  u32x4 aq[4];
+  int asc[4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int head = 32 * mt + col;
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t qr = (int64_t)row * 64 + 16 * mt + col;
     if (!MX) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(qI + ((int64_t)row * 64 + head) * 256 + 128 * half);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) afr[mt][ks] = __builtin_bit_cast(bf16x8, p[ks]);
+      for (int ks = 0; ks < (MX ? 1 : 4); ++ks)
+        afr[mt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qI + qr * 256 + 64 * ks + 16 * kg));
     } else {
-      const int64_t qr = (int64_t)row * 64 + head;
-      const u32x4* p = reinterpret_cast<const u32x4*>(qI + qr * 64 + 32 * half);
-      const u32x4 w0 = p[0], w1 = p[1];
-      const float s0 = exp2i((int)qI_scale[qr * 4 + 2 * half] - 127);
-      const float s1 = exp2i((int)qI_scale[qr * 4 + 2 * half + 1] - 127);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) afr[mt][ks] = e2m1x8_to_bf16(w0[ks], s0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) afr[mt][4 + ks] = e2m1x8_to_bf16(w1[ks], s1);
+      aq[mt] = *reinterpret_cast<const u32x4*>(qI + qr * 64 + 16 * kg);
+      asc[mt] = (int)(*reinterpret_cast<const uint32_t*>(qI_scale + qr * 4) >> (8 * kg));
     }
   }
-  // weights of the head rows this lane's accumulators hold:
-  // register r of tile mt is head 32*mt + 8*(r/4) + 4*half + r%4
-  float wr[2][16];
+  // weights of the head rows this lane's accumulators hold: register r of
+  // tile mt is head 16*mt + 4*kg + r
+  float wr[4][4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      wr[mt][r] = w[(int64_t)row * 64 + 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3)];
+    for (int r = 0; r < 4; ++r) wr[mt][r] = w[(int64_t)row * 64 + 16 * mt + 4 * kg + r];
 
-  // raw key bytes of one 32-entry sub-tile (bf16: 128 B per lane; MXFP4: 32 B
-  // of codes + the row's 4 scale bytes), prefetched one sub-tile ahead
   struct Raw {
-    u32x4 v[MX ? 2 : 8];
-    uint32_t sc;
+    u32x4 v[MX ? G : 4 * G];
+    uint32_t sc[MX ? G : 1];
   };
   auto fetch = [&](int base, Raw& r) {
-    const int n = base + col;
-    const int64_t kr = (int64_t)b * Nmax + (n < e1 ? n : e0);
-    if (!MX) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(kI + kr * 256 + 128 * half);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) r.v[ks] = p[ks];
-      r.sc = 0;
-    } else {
-      const u32x4* p = reinterpret_cast<const u32x4*>(kI + kr * 64 + 32 * half);
-      r.v[0] = p[0];
-      r.v[1] = p[1];
-      r.sc = *reinterpret_cast<const uint32_t*>(kI_scale + kr * 4);
+    for (int g = 0; g < G; ++g) {
+      const int n = base + 16 * g + col;
+      const int64_t kr = (int64_t)b * Nmax + (n < e1 ? n : e0);
+      if (!MX) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          r.v[4 * g + ks] = *reinterpret_cast<const u32x4*>(kI + kr * 256 + 64 * ks + 16 * kg);
+      } else {
+        r.v[g] = *reinterpret_cast<const u32x4*>(kI + kr * 64 + 16 * kg);
+        r.sc[g] = *reinterpret_cast<const uint32_t*>(kI_scale + kr * 4);
+      }
     }
   };
-  constexpr int STEP = IDX_WAVES * IDX_SUB;
-  Raw cur, nxt;
-  int base = e0 + wave * IDX_SUB;
-  if (base < e1) fetch(base, cur);
-  for (; base < e1; base += STEP) {
-    if (base + STEP < e1) fetch(base + STEP, nxt);
-    bf16x8 bfr[8];
-    if (!MX) {
+  auto process = [&](const Raw& r, int base) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) bfr[ks] = __builtin_bit_cast(bf16x8, cur.v[ks]);
-    } else {
-      const float s0 = exp2i((int)((cur.sc >> (16 * half)) & 0xFFu) - 127);
-      const float s1 = exp2i((int)((cur.sc >> (16 * half + 8)) & 0xFFu) - 127);
+    for (int g = 0; g < G; ++g) {
+      f32x4 acc[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bfr[ks] = e2m1x8_to_bf16(cur.v[0][ks], s0);
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!MX) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bfr[4 + ks] = e2m1x8_to_bf16(cur.v[1][ks], s1);
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 bk = __builtin_bit_cast(bf16x8, r.v[4 * g + ks]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][MX ? 0 : ks], bk, acc[mt], 0, 0, 0);
+        }
+      } else {
+        const i32x8 bk = widen(r.v[g]);
+        const int bs = (int)(r.sc[MX ? g : 0] >> (8 * kg));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(aq[mt]), bk, acc[mt], 4, 4, 0, asc[mt], 0, bs);
+      }
+      float sc = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], fmaxf(acc[mt][q], 0.f), sc);
+      sc += __shfl_xor(sc, 16);
+      sc += __shfl_xor(sc, 32);
+      const int n = base + 16 * g + col;
+      if (kg == 0 && n < e1) {
+        const int64_t o = (int64_t)row * Nmax + n;
+        if (score_bf16)
+          reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(sc);
+        else
+          reinterpret_cast<float*>(scores)[o] = sc;
+      }
     }
-    f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[0][ks], bfr[ks], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[1][ks], bfr[ks], acc1, 0, 0, 0);
-    }
-    float sc = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc = fmaf(wr[0][r], fmaxf(acc0[r], 0.f), sc);
-      sc = fmaf(wr[1][r], fmaxf(acc1[r], 0.f), sc);
-    }
-    sc += __shfl_xor(sc, 32);
-    const int n = base + col;
-    if (half == 0 && n < e1) {
-      const int64_t o = (int64_t)row * Nmax + n;
-      if (score_bf16)
-        reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(sc);
-      else
-        reinterpret_cast<float*>(scores)[o] = sc;
-    }
-    cur = nxt;
+  };
+  constexpr int STEP = IDX_WAVES * 16 * G;
+  int base = e0 + wave * 16 * G;
+  Raw r0, r1, r2;
+  if (base < e1) fetch(base, r0);
+  if (base + STEP < e1) fetch(base + STEP, r1);
+  for (; base < e1; base += 3 * STEP) {
+    if (base + 2 * STEP < e1) fetch(base + 2 * STEP, r2);
+    process(r0, base);
+    if (base + STEP >= e1) break;
+    if (base + 3 * STEP < e1) fetch(base + 3 * STEP, r0);
+    process(r1, base + STEP);
+    if (base + 2 * STEP >= e1) break;
+    if (base + 4 * STEP < e1) fetch(base + 4 * STEP, r1);
+    process(r2, base + 2 * STEP);
   }
 }
 
@@ -197,11 +208,12 @@ hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_
   if (rows == 0 || Nmax == 0) return hipSuccess;
   const int sbf = score_t == CSA_BF16;
   if ((in_t == CSA_BF16 || in_t == CSA_MXFP4) && nI == 64 && cI == 128) {
-    // about three blocks per CU over the whole call; a block covers a
-    // multiple of 128 entries (4 waves x 32)
-    const int64_t want = ((int64_t)Nmax * rows + 767) / 768;
-    int epb = (int)(((want + 127) / 128) * 128);
-    epb = epb < 256 ? 256 : (epb > 8192 ? 8192 : epb);
+    // about two resident blocks per CU over the whole call; a block covers a
+    // multiple of one step of its 4 waves (bf16 128 entries, MXFP4 512)
+    const int step = in_t == CSA_MXFP4 ? 512 : 128;
+    const int64_t want = ((int64_t)Nmax * rows + 511) / 512;
+    int epb = (int)(((want + step - 1) / step) * step);
+    epb = epb < 2 * step ? 2 * step : (epb > 8192 ? 8192 : epb);
     dim3 grid((unsigned)(((int64_t)Nmax + epb - 1) / epb * rows));
     if (in_t == CSA_BF16)
       hipLaunchKernelGGL(indexer_mfma_kernel<false>, grid, dim3(IDX_WAVES * 64), 0, s,

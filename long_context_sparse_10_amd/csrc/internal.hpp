@@ -33,9 +33,11 @@ hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_
                           int m, void* scores, csa_dtype score_t, hipStream_t s);
 
 // topk.hip --------------------------------------------------------------------
+// workspace bytes top-k needs (0 for rows of up to 16384 entries)
+size_t topk_workspace(int B, int Tq, int Nmax);
 hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int Nmax, int m, int k,
-                       int32_t* idx, hipStream_t s);
+                       int32_t* idx, void* ws, hipStream_t s);
 
 // attend.hip -------------------------------------------------------------------
 struct AttendArgs {

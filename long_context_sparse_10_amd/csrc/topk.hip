@@ -7,10 +7,13 @@
 // (until k are taken) are written in ascending entry order, so ties go to the
 // lower index, and rows with fewer than k visible entries are padded with -1.
 //
-// Rows of up to KPT * blockDim entries keep their keys in registers: thread t
-// owns the contiguous entries [KPT t, KPT t + KPT), every radix pass works on
-// registers, and the ordered compaction needs a single block-wide scan.
-// Longer rows stream their keys from memory on every pass.
+// Rows of up to 16 * 1024 entries run in one block per row with the keys in
+// registers: thread t owns the contiguous entries [16 t, 16 t + 16), every
+// radix pass works on registers, and the ordered compaction needs a single
+// block-wide scan.  Longer rows (few decode rows over 2^18 entries) spread over
+// many blocks per row: per-block digit histograms, a per-row reduction that
+// fixes the digit, and after the last digit per-block counts and an ordered
+// emit at each block's offset.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -28,6 +31,40 @@ template <bool BF16>
 __device__ __forceinline__ uint32_t load_key(const void* scores, int64_t i) {
   if (BF16) return bf16_key(reinterpret_cast<const uint16_t*>(scores)[i]);
   return f32_key(reinterpret_cast<const uint32_t*>(scores)[i]);
+}
+
+// the 16 keys of entries [s0, s0 + 16) of a row (0 for s >= nv); whole
+// 16-byte loads when the chunk lies inside the row's Nmax entries
+template <bool BF16>
+__device__ __forceinline__ void load_keys16(const void* srow, int s0, int nv, int Nmax,
+                                            uint32_t* key) {
+  if (s0 + 16 <= Nmax) {
+    if (BF16) {
+      const u32x4* p = reinterpret_cast<const u32x4*>((const uint16_t*)srow + s0);
+      const u32x4 a = p[0], b = p[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        key[2 * i] = bf16_key(a[i] & 0xFFFFu);
+        key[2 * i + 1] = bf16_key(a[i] >> 16);
+        key[8 + 2 * i] = bf16_key(b[i] & 0xFFFFu);
+        key[8 + 2 * i + 1] = bf16_key(b[i] >> 16);
+      }
+    } else {
+      const u32x4* p = reinterpret_cast<const u32x4*>((const uint32_t*)srow + s0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 v = p[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) key[4 * j + i] = f32_key(v[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) key[i] = (s0 + i < Nmax) ? load_key<BF16>(srow, s0 + i) : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (s0 + i >= nv) key[i] = 0u;
 }
 
 // exclusive block scan of one int per thread; *total gets the block sum.
@@ -85,11 +122,11 @@ __device__ __forceinline__ void find_digit(const int* hist, int nbins, int remai
   }
 }
 
-template <bool BF16, int KPT>
+template <bool BF16>
 __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ scores,
                                                     const int32_t* __restrict__ q_pos,
                                                     const int32_t* __restrict__ n_entries, int Tq,
-                                                    int Nmax, int m, int k,
+                                                    int Nmax, int m, int k, int vec,
                                                     int32_t* __restrict__ idx) {
   __shared__ int hist[2048];
   __shared__ int scan_ws[16];
@@ -105,14 +142,14 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
     for (int i = tid; i < k; i += nt) out[i] = i < nv ? i : -1;
     return;
   }
-  constexpr int KR = KPT > 0 ? KPT : 1;
-  const bool in_regs = KPT > 0 && nv <= KR * nt;
-  // ---- keys in registers: contiguous chunk per thread
-  uint32_t key[KR];
-  const int s0 = tid * KR;
-  if (in_regs) {
+  // ---- keys in registers: thread t owns entries [16 t, 16 t + 16)
+  uint32_t key[16];
+  const int s0 = tid * 16;
+  if (vec) {
+    load_keys16<BF16>(srow, s0, nv, Nmax, key);
+  } else {
 #pragma unroll
-    for (int i = 0; i < KR; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
+    for (int i = 0; i < 16; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
   }
   // ---- radix select: digits of 11/11/10 bits (fp32 keys) or 8/8 bits (bf16 keys)
   uint32_t prefix = 0u, pmask = 0u;
@@ -125,17 +162,9 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
     const uint32_t dmask = (uint32_t)nbins - 1u;
     for (int i = tid; i < nbins; i += nt) hist[i] = 0;
     __syncthreads();
-    if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < KR; ++i)
-        if (s0 + i < nv && (key[i] & pmask) == prefix)
-          atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
-    } else {
-      for (int s = tid; s < nv; s += nt) {
-        const uint32_t kk = load_key<BF16>(srow, s);
-        if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & dmask], 1);
-      }
-    }
+    for (int i = 0; i < 16; ++i)
+      if (s0 + i < nv && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
     __syncthreads();
     find_digit(hist, nbins, remaining, &sh_digit, &sh_above);
     __syncthreads();
@@ -145,66 +174,289 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
   }
   const uint32_t kstar = prefix;
   const int need_eq = remaining;  // entries equal to K* to take, lowest index first
-  // ---- ordered compaction
-  if (in_regs) {
-    int gt = 0, eq = 0;
+  // ---- ordered compaction: one block-wide scan of (above, equal) counts
+  int gt = 0, eq = 0;
 #pragma unroll
-    for (int i = 0; i < KR; ++i) {
-      const bool ok = s0 + i < nv;
-      gt += (ok && key[i] > kstar) ? 1 : 0;
-      eq += (ok && key[i] == kstar) ? 1 : 0;
-    }
-    int total;
-    const int excl = block_scan_excl(gt | (eq << 16), scan_ws, &total);
-    int gt_before = excl & 0xFFFF, eq_before = excl >> 16;
+  for (int i = 0; i < 16; ++i) {
+    const bool ok = s0 + i < nv;
+    gt += (ok && key[i] > kstar) ? 1 : 0;
+    eq += (ok && key[i] == kstar) ? 1 : 0;
+  }
+  int total;
+  const int excl = block_scan_excl(gt | (eq << 16), scan_ws, &total);
+  int gt_before = excl & 0xFFFF, eq_before = excl >> 16;
 #pragma unroll
-    for (int i = 0; i < KR; ++i) {
-      const bool ok = s0 + i < nv;
-      const bool g = ok && key[i] > kstar, e = ok && key[i] == kstar;
-      if (g || (e && eq_before < need_eq)) {
-        const int pos = gt_before + min(eq_before, need_eq);
-        if (pos < k) out[pos] = s0 + i;
-      }
-      gt_before += g ? 1 : 0;
-      eq_before += e ? 1 : 0;
-    }
-  } else {
-    int run_gt = 0, run_eq = 0;
-    for (int base = 0; base < nv; base += nt) {
-      const int s = base + tid;
-      uint32_t kk = 0;
-      if (s < nv) kk = load_key<BF16>(srow, s);
-      const int g = (s < nv) && kk > kstar;
-      const int e = (s < nv) && kk == kstar;
-      int total;
-      const int excl = block_scan_excl(g | (e << 16), scan_ws, &total);
-      const int gt_before = run_gt + (excl & 0xFFFF), eq_before = run_eq + (excl >> 16);
+  for (int i = 0; i < 16; ++i) {
+    const bool ok = s0 + i < nv;
+    const bool g = ok && key[i] > kstar, e = ok && key[i] == kstar;
+    if (g || (e && eq_before < need_eq)) {
       const int pos = gt_before + min(eq_before, need_eq);
-      if ((g || (e && eq_before < need_eq)) && pos < k) out[pos] = s;
-      run_gt += total & 0xFFFF;
-      run_eq += total >> 16;
+      if (pos < k) out[pos] = s0 + i;
+    }
+    gt_before += g ? 1 : 0;
+    eq_before += e ? 1 : 0;
+  }
+}
+
+// ------------------------------------------------------------------ long rows
+// Multi-block radix select.  Row r is cut into P slices of TKM_SLICE entries,
+// one 256-thread block each (16 keys per thread in registers).  Per digit:
+// topk_hist_kernel writes each slice's histogram of the digit among the keys
+// that match the row's current prefix; topk_reduce_kernel sums them, locates
+// the digit holding the remaining rank and extends the prefix.  After the last
+// digit the prefix is the k-th largest key K* and `remaining` the number of
+// keys equal to K* to take; topk_count_kernel counts each slice's keys above /
+// equal to K* and topk_emit_kernel writes the slice's selection at its offset.
+// Workspace (ints): row state [rows][4], histograms [rows][P][2048], counts
+// [rows][P][2].
+constexpr int TKM_THREADS = 256;
+constexpr int TKM_SLICE = 16 * TKM_THREADS;
+
+struct TkRow {
+  uint32_t prefix, pmask;
+  int remaining;
+  int pad;
+};
+
+__device__ __forceinline__ int row_visible(const int32_t* q_pos, const int32_t* n_entries, int row,
+                                           int Tq, int Nmax, int m) {
+  return min(min(n_entries[row / Tq], Nmax), (q_pos[row] + 1) / m);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(TKM_THREADS) void topk_hist_kernel(
+    const void* __restrict__ scores, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int Nmax, int m, int k, int vec, int P,
+    int shift, int width, const TkRow* __restrict__ st, int* __restrict__ hist) {
+  __shared__ int h[2048];
+  const int row = blockIdx.x / P, p = blockIdx.x % P, tid = threadIdx.x;
+  const int nv = row_visible(q_pos, n_entries, row, Tq, Nmax, m);
+  if (nv <= k) return;
+  const int nbins = 1 << width;
+  const uint32_t dmask = (uint32_t)nbins - 1u;
+  const uint32_t prefix = st ? st[row].prefix : 0u, pmask = st ? st[row].pmask : 0u;
+  for (int i = tid; i < nbins; i += TKM_THREADS) h[i] = 0;
+  __syncthreads();
+  const int s0 = p * TKM_SLICE + 16 * tid;
+  if (s0 < nv) {
+    const void* srow = BF16 ? (const void*)((const uint16_t*)scores + (int64_t)row * Nmax)
+                            : (const void*)((const uint32_t*)scores + (int64_t)row * Nmax);
+    uint32_t key[16];
+    if (vec) {
+      load_keys16<BF16>(srow, s0, nv, Nmax, key);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (s0 + i < nv && (key[i] & pmask) == prefix) atomicAdd(&h[(key[i] >> shift) & dmask], 1);
+  }
+  __syncthreads();
+  int* out = hist + ((int64_t)row * P + p) * 2048;
+  for (int i = tid; i < nbins; i += TKM_THREADS) out[i] = h[i];
+}
+
+// one block per row: sum the slice histograms, fix the digit
+__global__ __launch_bounds__(1024) void topk_reduce_kernel(
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int Tq, int Nmax,
+    int m, int k, int P, int shift, int width, int first, TkRow* __restrict__ st,
+    const int* __restrict__ hist) {
+  __shared__ int h[2048];
+  __shared__ uint32_t sh_digit;
+  __shared__ int sh_above;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int nv = row_visible(q_pos, n_entries, row, Tq, Nmax, m);
+  if (nv <= k) return;
+  const int nbins = 1 << width;
+  const int* hr = hist + (int64_t)row * P * 2048;
+  for (int i = tid; i < nbins; i += 1024) {
+    int acc = 0;
+    for (int p = 0; p < P; ++p) acc += hr[(int64_t)p * 2048 + i];
+    h[i] = acc;
+  }
+  const TkRow cur = first ? TkRow{0u, 0u, k, 0} : st[row];
+  __syncthreads();
+  find_digit(h, nbins, cur.remaining, &sh_digit, &sh_above);
+  __syncthreads();
+  if (tid == 0) {
+    TkRow nx;
+    nx.prefix = cur.prefix | (sh_digit << shift);
+    nx.pmask = cur.pmask | ((uint32_t)(nbins - 1) << shift);
+    nx.remaining = cur.remaining - sh_above;
+    nx.pad = 0;
+    st[row] = nx;
+  }
+}
+
+// per slice: keys above K* and keys equal to K*
+template <bool BF16>
+__global__ __launch_bounds__(TKM_THREADS) void topk_count_kernel(
+    const void* __restrict__ scores, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int Nmax, int m, int k, int vec, int P,
+    const TkRow* __restrict__ st, int* __restrict__ cnt) {
+  __shared__ int scan_ws[16];
+  const int row = blockIdx.x / P, p = blockIdx.x % P, tid = threadIdx.x;
+  const int nv = row_visible(q_pos, n_entries, row, Tq, Nmax, m);
+  if (nv <= k) return;
+  const uint32_t kstar = st[row].prefix;
+  const int s0 = p * TKM_SLICE + 16 * tid;
+  int gt = 0, eq = 0;
+  if (s0 < nv) {
+    const void* srow = BF16 ? (const void*)((const uint16_t*)scores + (int64_t)row * Nmax)
+                            : (const void*)((const uint32_t*)scores + (int64_t)row * Nmax);
+    uint32_t key[16];
+    if (vec) {
+      load_keys16<BF16>(srow, s0, nv, Nmax, key);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      gt += (s0 + i < nv && key[i] > kstar) ? 1 : 0;
+      eq += (s0 + i < nv && key[i] == kstar) ? 1 : 0;
     }
   }
+  int total;
+  block_scan_excl(gt | (eq << 16), scan_ws, &total);
+  if (tid == 0) {
+    int* c = cnt + ((int64_t)row * P + p) * 2;
+    c[0] = total & 0xFFFF;
+    c[1] = total >> 16;
+  }
+}
+
+// per slice: ordered write of the slice's selection at its offset; rows with
+// N(q) <= k take all their visible entries
+template <bool BF16>
+__global__ __launch_bounds__(TKM_THREADS) void topk_emit_kernel(
+    const void* __restrict__ scores, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int Nmax, int m, int k, int vec, int P,
+    const TkRow* __restrict__ st, const int* __restrict__ cnt, int32_t* __restrict__ idx) {
+  __shared__ int scan_ws[16];
+  __shared__ int sh_gt, sh_eq;
+  const int row = blockIdx.x / P, p = blockIdx.x % P, tid = threadIdx.x;
+  const int nv = row_visible(q_pos, n_entries, row, Tq, Nmax, m);
+  int32_t* out = idx + (int64_t)row * k;
+  if (nv <= k) {
+    for (int i = p * TKM_THREADS + tid; i < k; i += P * TKM_THREADS) out[i] = i < nv ? i : -1;
+    return;
+  }
+  const uint32_t kstar = st[row].prefix;
+  const int need_eq = st[row].remaining;
+  // offsets: selections of the slices before this one
+  if (tid < 64) {
+    int g = 0, e = 0;
+    for (int q = tid; q < p; q += 64) {
+      g += cnt[((int64_t)row * P + q) * 2];
+      e += cnt[((int64_t)row * P + q) * 2 + 1];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      g += __shfl_xor(g, o);
+      e += __shfl_xor(e, o);
+    }
+    if (tid == 0) {
+      sh_gt = g;
+      sh_eq = e;
+    }
+  }
+  __syncthreads();
+  const int s0 = p * TKM_SLICE + 16 * tid;
+  uint32_t key[16];
+  const void* srow = BF16 ? (const void*)((const uint16_t*)scores + (int64_t)row * Nmax)
+                          : (const void*)((const uint32_t*)scores + (int64_t)row * Nmax);
+  if (s0 < nv) {
+    if (vec) {
+      load_keys16<BF16>(srow, s0, nv, Nmax, key);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
+    }
+  }
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool ok = s0 + i < nv;
+    gt += (ok && key[i] > kstar) ? 1 : 0;
+    eq += (ok && key[i] == kstar) ? 1 : 0;
+  }
+  int total;
+  const int excl = block_scan_excl(gt | (eq << 16), scan_ws, &total);
+  int gt_before = sh_gt + (excl & 0xFFFF), eq_before = sh_eq + (excl >> 16);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool ok = s0 + i < nv;
+    const bool g = ok && key[i] > kstar, e = ok && key[i] == kstar;
+    if (g || (e && eq_before < need_eq)) {
+      const int pos = gt_before + min(eq_before, need_eq);
+      if (pos < k) out[pos] = s0 + i;
+    }
+    gt_before += g ? 1 : 0;
+    eq_before += e ? 1 : 0;
+  }
+}
+
+static bool topk_multiblock(int Nmax) { return Nmax > 16 * 1024; }
+
+size_t topk_workspace(int B, int Tq, int Nmax) {
+  if (!topk_multiblock(Nmax)) return 0;
+  const int64_t rows = (int64_t)B * Tq;
+  const int64_t P = (Nmax + TKM_SLICE - 1) / TKM_SLICE;
+  return (size_t)(rows * 4 + rows * P * 2048 + rows * P * 2) * sizeof(int);
 }
 
 hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int Nmax, int m, int k,
-                       int32_t* idx, hipStream_t s) {
+                       int32_t* idx, void* ws, hipStream_t s) {
   const int rows = B * Tq;
   if (rows == 0) return hipSuccess;
-  const int threads = Nmax > 4096 ? 1024 : (Nmax > 1024 ? 256 : 64);
-  const int kpt = (Nmax + threads - 1) / threads;
   const bool bf = score_t == CSA_BF16;
-#define CSA_TOPK(BF, KP)                                                                   \
-  hipLaunchKernelGGL((topk_kernel<BF, KP>), dim3(rows), dim3(threads), 0, s, scores, q_pos, \
-                     n_entries, Tq, Nmax, m, k, idx)
-  // register-resident rows: per-thread counts stay below 2^16 for the packed scan
-  if (kpt <= 16) {
-    if (bf) CSA_TOPK(true, 16); else CSA_TOPK(false, 16);
-  } else {
-    if (bf) CSA_TOPK(true, 0); else CSA_TOPK(false, 0);
+  // whole 16-byte key loads need 16-byte aligned rows
+  const int vec = ((uintptr_t)scores % 16 == 0) && (bf ? Nmax % 8 == 0 : Nmax % 4 == 0);
+  if (topk_multiblock(Nmax)) {
+    const int P = (Nmax + TKM_SLICE - 1) / TKM_SLICE;
+    TkRow* st = reinterpret_cast<TkRow*>(ws);
+    int* hist = reinterpret_cast<int*>(ws) + (int64_t)rows * 4;
+    int* cnt = hist + (int64_t)rows * P * 2048;
+    const dim3 g((unsigned)((int64_t)rows * P)), t(TKM_THREADS);
+    // digits: bf16 keys 8 + 8 bits, fp32 keys 11 + 11 + 10 bits
+    int shift = bf ? 16 : 32, first = 1;
+    while (shift > 0) {
+      const int width = bf ? 8 : (shift == 32 || shift == 21 ? 11 : 10);
+      shift -= width;
+      if (bf)
+        hipLaunchKernelGGL(topk_hist_kernel<true>, g, t, 0, s, scores, q_pos, n_entries, Tq, Nmax,
+                           m, k, vec, P, shift, width, first ? nullptr : st, hist);
+      else
+        hipLaunchKernelGGL(topk_hist_kernel<false>, g, t, 0, s, scores, q_pos, n_entries, Tq, Nmax,
+                           m, k, vec, P, shift, width, first ? nullptr : st, hist);
+      hipLaunchKernelGGL(topk_reduce_kernel, dim3(rows), dim3(1024), 0, s, q_pos, n_entries, Tq,
+                         Nmax, m, k, P, shift, width, first, st, hist);
+      first = 0;
+    }
+    if (bf) {
+      hipLaunchKernelGGL(topk_count_kernel<true>, g, t, 0, s, scores, q_pos, n_entries, Tq, Nmax,
+                         m, k, vec, P, st, cnt);
+      hipLaunchKernelGGL(topk_emit_kernel<true>, g, t, 0, s, scores, q_pos, n_entries, Tq, Nmax,
+                         m, k, vec, P, st, cnt, idx);
+    } else {
+      hipLaunchKernelGGL(topk_count_kernel<false>, g, t, 0, s, scores, q_pos, n_entries, Tq, Nmax,
+                         m, k, vec, P, st, cnt);
+      hipLaunchKernelGGL(topk_emit_kernel<false>, g, t, 0, s, scores, q_pos, n_entries, Tq, Nmax,
+                         m, k, vec, P, st, cnt, idx);
+    }
+    return hipGetLastError();
   }
-#undef CSA_TOPK
+  // one block per row, 16 keys per thread (counts stay below 2^16 for the packed scan)
+  const int threads = Nmax > 4096 ? 1024 : (Nmax > 1024 ? 256 : 64);
+  if (bf)
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(threads), 0, s, scores, q_pos,
+                       n_entries, Tq, Nmax, m, k, vec, idx);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(rows), dim3(threads), 0, s, scores, q_pos,
+                       n_entries, Tq, Nmax, m, k, vec, idx);
   return hipGetLastError();
 }
 

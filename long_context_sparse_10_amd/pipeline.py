@@ -69,6 +69,7 @@ class Decode:
     idx: Optional[torch.Tensor] = None
     out: Optional[torch.Tensor] = None
     ws: Optional[torch.Tensor] = None
+    ws_topk: Optional[torch.Tensor] = None
     extra: dict = field(default_factory=dict)
 
 
@@ -122,8 +123,8 @@ def decode_indexer(d: Decode, stream=None):
 
 def decode_topk(d: Decode, stream=None):
     sp = d.spec
-    C.topk_select(d.scores, d.score_fmt, d.q_pos, d.n_entries, d.B, 1, d.Nmax, sp.m, sp.k, d.idx,
-                  None, stream)
+    d.ws_topk = C.topk_select(d.scores, d.score_fmt, d.q_pos, d.n_entries, d.B, 1, d.Nmax, sp.m,
+                              sp.k, d.idx, d.ws_topk, stream)
 
 
 def decode_attend(d: Decode, idx=None, stream=None):

@@ -53,5 +53,16 @@ def score_error_bound(qI, w, kI, nv, rel=1e-5):
     return rel * (np.abs(kI[:nv]) @ np.abs(qI).T) @ np.abs(w)
 
 
+def mx_score_bound(inp, b, ref, nv):
+    """Bound on |GPU bf16 score - quantised-oracle bf16 score| for MXFP4 keys:
+    the fp32 accumulation error of the exact E2M1 products plus one bf16 step
+    (the two sides may round to neighbouring bf16 values)."""
+    from oracle import pipeline as OP
+    kI, _, _ = OP.mxfp4_values(inp["kI"][b][:nv])
+    qI, _, _ = OP.mxfp4_values(inp["qI"][b, 0])
+    e = score_error_bound(qI, inp["w"][b, 0], kI, nv)
+    return bf16_ulp(np.abs(ref) + e) + e
+
+
 def report(name, **kv):
     print(f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in kv.items()), flush=True)

@@ -118,6 +118,10 @@ def test_topk_validation_and_workspace():
     need = ctypes.c_size_t(99)
     assert f(D, L.F32, D, D, 2, 1, 100, 4, 8, D, None, ctypes.byref(need), None) == _lib.OK
     assert need.value == 0
+    # rows longer than 16384 entries run multi-block and need a workspace
+    assert f(D, L.BF16, D, D, 8, 1, 262144, 4, 1024, D, None, ctypes.byref(need), None) == _lib.OK
+    assert need.value >= 8 * 64 * 2048 * 4
+    assert f(D, L.BF16, D, D, 8, 1, 262144, 4, 1024, D, None, None, None) == _lib.ERR_WORKSPACE
     assert f(D, L.F32, D, D, 2, 1, 100, 4, 0, D, None, None, None) == _lib.ERR_INVALID
     assert f(D, L.FP8MIX, D, D, 2, 1, 100, 4, 8, D, None, None, None) == _lib.ERR_UNSUPPORTED
     assert f(None, L.F32, D, D, 2, 1, 100, 4, 8, D, None, None, None) == _lib.ERR_INVALID

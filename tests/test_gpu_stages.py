@@ -14,7 +14,7 @@ from long_context_sparse_10_amd import pipeline as G
 from oracle import csa as O
 from oracle import formats as F
 from oracle import pipeline as OP
-from tests.gpu_util import (bf16_ulp, decode_rows, dev, e4m3_ulp, np64, report,
+from tests.gpu_util import (bf16_ulp, decode_rows, mx_score_bound, dev, e4m3_ulp, np64, report,
                             score_error_bound)
 
 pytestmark = pytest.mark.gpu
@@ -169,8 +169,9 @@ def test_indexer_mxfp4_matches_quantized_oracle():
         ref, nv = OP.decode_scores(inp, b)          # quantised fp64 scores, rounded to bf16
         err = np.abs(S[b, 0, :nv] - ref)
         ulp = bf16_ulp(ref)
-        report("indexer mxfp4", b=b, nv=nv, ulps=float((err / ulp).max()))
-        assert np.all(err <= ulp + 1e-30)
+        report("indexer mxfp4", b=b, nv=nv, ulps=float((err / ulp).max()) if nv else 0.0,
+               exact=float(np.mean(err == 0)) if nv else 1.0)
+        assert np.all(err <= mx_score_bound(inp, b, ref, nv) + 1e-30)
 
 
 def test_indexer_generic_f32_and_causal_prefill():
@@ -209,7 +210,8 @@ def _score_rows(rng, kind, rows, N):
 
 @pytest.mark.parametrize("kind", ["ties", "bf16", "normal"])
 @pytest.mark.parametrize("N,k,m", [(16384, 1024, 4), (3000, 1024, 4), (700, 32, 4),
-                                   (1025, 1024, 4), (40000, 512, 4)])
+                                   (1025, 1024, 4), (40000, 512, 4), (20001, 100, 4),
+                                   (262144, 1024, 4)])
 def test_topk_bit_exact(kind, N, k, m):
     """Same score arrays (from the seeded generator) on both sides: the index
     sets are integer results and must be identical, ties included."""
@@ -224,6 +226,8 @@ def test_topk_bit_exact(kind, N, k, m):
     dt = torch.bfloat16 if fmt == L.BF16 else torch.float32
     st = torch.from_numpy(S).to(d).to(dt).reshape(rows, 1, N)
     idx = torch.empty(rows, 1, k, dtype=torch.int32, device=d)
+    # rows over 16384 entries take the multi-block path (workspace); the odd
+    # length exercises the unaligned key loads
     L.topk_select(st, fmt, torch.from_numpy(qpos).reshape(rows, 1).to(d),
                   torch.from_numpy(n_ent).to(d), rows, 1, N, m, k, idx)
     got = idx.cpu().numpy()[:, 0]
