@@ -35,6 +35,21 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP/s"
 
+# HBM traffic of the roofline kernel, per launch: rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch), each scaled by bytes / counter of a plain copy
+# of known size (--copy-probe).  An entry holds for the kernel source it was
+# taken on (sha256 of the .hip file); after any change it reports null.
+TRAFFIC = {
+    "decode_64k": dict(src="indexer.hip", sha256="95037799299b7ce7a02c010d03c983d2cb90de83799586718bc8b5f4a7419817",
+                fetch_kib=67664.5, write_kib=2048.5, fetch_scale=1.9998, write_scale=1.0),
+    "hca_decode_1m": dict(src="attend.hip", sha256="657d8f191ce02f313b6f8777d29aaf8cfecc35944588d12f263159a3950e66cf",
+                fetch_kib=70997.8, write_kib=32896.0, fetch_scale=1.9998, write_scale=1.0),
+    "decode_1m_fp4": dict(src="indexer.hip", sha256="95037799299b7ce7a02c010d03c983d2cb90de83799586718bc8b5f4a7419817",
+                fetch_kib=69898.2, write_kib=4096.5, fetch_scale=1.9998, write_scale=1.0),
+    "prefill_32k": dict(src="attend.hip", sha256="657d8f191ce02f313b6f8777d29aaf8cfecc35944588d12f263159a3950e66cf",
+                fetch_kib=3295163.5, write_kib=2097207.2, fetch_scale=1.9998, write_scale=1.0),
+}
+
 
 # ------------------------------------------------------------------ algorithmic bytes
 def decode_bytes(sp, N):
@@ -141,35 +156,46 @@ def run_decode(args, torch, I, G):
     torch.cuda.synchronize()
     print(f"[bench] {args.copies} cache copies resident", file=sys.stderr, flush=True)
     kinds = ["indexer", "topk", "attend"] if sp.kind == "decode" else ["attend"]
+    call = {"indexer": G.decode_indexer, "topk": G.decode_topk,
+            "attend": lambda c, s: G.decode_attend(c, stream=s)}
+    # per-kernel launch time: each call back to back over the rotated copies
+    # (the queue stays full, so an event pair brackets kernel time only)
+    avg = {}
+    for kind in kinds:
+        reps = max(args.steps, 12)
+        with torch.cuda.stream(stream):
+            for i in range(len(copies)):
+                call[kind](copies[i], stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                call[kind](copies[i % len(copies)], stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        avg[kind] = e0.elapsed_time(e1) * 1e3 / reps
+    # the step: one HIP graph per cache copy (captured after the eager warm-up,
+    # which also sized every workspace), replayed in rotation
+    graphs = []
+    for c in copies:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            G.decode_step(c, stream)
+        graphs.append(gr)
+    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
-            G.decode_step(copies[i % len(copies)], stream)
+            graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kinds) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
     with torch.cuda.stream(stream):
+        e0.record(stream)
         for i in range(args.steps):
-            c = copies[i % len(copies)]
-            e = ev[i]
-            e[0].record(stream)
-            if sp.kind == "decode":
-                G.decode_indexer(c, stream)
-                e[1].record(stream)
-                G.decode_topk(c, stream)
-                e[2].record(stream)
-                G.decode_attend(c, stream=stream)
-                e[3].record(stream)
-            else:
-                G.decode_attend(c, stream=stream)
-                e[1].record(stream)
+            graphs[i % len(graphs)].replay()
+        e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    per = {k: [] for k in kinds}
-    for e in ev:
-        for j, k in enumerate(kinds):
-            per[k].append(e[j].elapsed_time(e[j + 1]) * 1e3)     # us
-    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    gpu_ms = e0.elapsed_time(e1)
     ms_step = elapsed / args.steps * 1e3
     N = inp["Nmax"]
     by = decode_bytes(sp, N)
@@ -191,7 +217,8 @@ def run_decode(args, torch, I, G):
                       frac=achieved / HBM_PEAK_GBS, traffic=None,
                       algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=avg[dom]),
         step=dict(algorithmic_bytes=by["total"] * sp.B, achieved_gbs=step_gbs,
-                  frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS,
+                  frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS, gpu_ms_per_step=gpu_ms / args.steps,
+                  launch="one HIP graph per cache copy",
                   kernel_us={k: round(v, 2) for k, v in avg.items()}),
     )
     return res, inp
@@ -262,6 +289,32 @@ def run_prefill(args, torch, I, G):
     return res, inp
 
 
+def kernel_traffic(config):
+    """Measured HBM bytes per launch of the roofline kernel, or None."""
+    t = TRAFFIC.get(config)
+    if t is None:
+        return None
+    import hashlib
+    src = os.path.join(ROOT, "long_context_sparse_10_amd", "csrc", t["src"])
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
+            return None
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
+
+def copy_probe(torch):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "dispatches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +324,8 @@ def main():
                     choices=["decode_64k", "hca_decode_1m", "decode_1m_fp4", "prefill_32k"])
     ap.add_argument("--copies", type=int, default=6, help="cache copies rotated (cold cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -278,6 +333,9 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     import csa_inputs as I
     from long_context_sparse_10_amd import pipeline as G
     if args.config == "prefill_32k":
@@ -285,6 +343,7 @@ def main():
         res, inp = run_prefill(args, torch, I, G)
     else:
         res, inp = run_decode(args, torch, I, G)
+    res["roofline"]["traffic"] = kernel_traffic(args.config)
     if not args.no_cpu_baseline:
         if args.config == "prefill_32k":
             rows = np.linspace(0, inp["T"] - 1, 64).astype(int)

@@ -270,10 +270,16 @@ __global__ __launch_bounds__(1024) void topk_reduce_kernel(
   if (nv <= k) return;
   const int nbins = 1 << width;
   const int* hr = hist + (int64_t)row * P * 2048;
-  for (int i = tid; i < nbins; i += 1024) {
+  // thread (bin, part): sums slices part, part + parts, ...; parts combine in LDS
+  const int parts = nbins >= 1024 ? 1 : 1024 / nbins;
+  for (int i = tid; i < nbins; i += 1024) h[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < nbins * parts; i += 1024) {
+    const int bin = i % nbins, part = i / nbins;
     int acc = 0;
-    for (int p = 0; p < P; ++p) acc += hr[(int64_t)p * 2048 + i];
-    h[i] = acc;
+#pragma unroll 8
+    for (int p = part; p < P; p += parts) acc += hr[(int64_t)p * 2048 + bin];
+    if (acc) atomicAdd(&h[bin], acc);
   }
   const TkRow cur = first ? TkRow{0u, 0u, k, 0} : st[row];
   __syncthreads();
