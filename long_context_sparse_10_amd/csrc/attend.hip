@@ -10,14 +10,15 @@
 // then n_win window slots for positions q-n_win+1 .. q (negative = empty).
 //
 // Kernels
-//  * attend_mfma_kernel   -- c = 512, heads a multiple of 16, bf16 or
-//    FP8/BF16 KV.  One block per (query row, slot split); wave w owns heads
-//    16w..16w+15 with its RMSNorm'd, RoPE'd query held as bf16 MFMA fragments.
-//    32-slot tiles of KV rows are gathered into LDS (double buffered, e4m3
-//    expanded to bf16 on the way), S = Q K^T and O += P V run on
+//  * attend_mfma_kernel   -- c = 512, heads a multiple of 64, bf16 or
+//    FP8/BF16 KV.  One 512-thread block per (query row, 64 heads, slot split):
+//    four loader waves gather 32-slot tiles of KV rows through a register ring
+//    into a double-buffered LDS tile (e4m3 expanded to bf16 on the way); four
+//    math waves of 16 heads run S^T = X Q^T and O^T += X^T P^T on
 //    v_mfma_f32_16x16x32_bf16 with an fp32 online softmax in registers.
 //    With one split the block finishes the output itself; otherwise it writes
-//    (m, l, O) partials and attend_combine_kernel merges the splits in order.
+//    per-split (m, l) and O / l (bf16) and attend_combine_kernel merges the
+//    splits in order.
 //  * attend_generic_kernel -- any shape / fp32: one wave per head, VALU.
 #include "common.hpp"
 #include "internal.hpp"
@@ -195,6 +196,7 @@ struct AttendSmem {
   int32_t slot[AT_TAB + 64];
   uint32_t vmask[AT_TAB / 32 + 2];
   float rcs[AT_C / 2][2];           // cos / sin of the query position for each RoPE pair
+  float qg[AT_C];                   // query RMSNorm gains
 };
 
 // load 8 consecutive elements (dims d..d+7) of a q row as fp32
@@ -252,7 +254,7 @@ __device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
 // One barrier per tile separates the two buffers.
 template <int KVF>
 __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt, int chunk,
-                                                         int nsplit, float* __restrict__ ws) {
+                                                         int nsplit, void* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) AttendSmem sm;
   const int hgroups = a.nh / 64;
   const int split = blockIdx.x % nsplit;
@@ -290,6 +292,8 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
     sm.rcs[u][0] = cs;
     sm.rcs[u][1] = sn;
   }
+  // ---- query RMSNorm gains (1 without a gain vector)
+  if (tid < AT_C) sm.qg[tid] = a.q_norm_w != nullptr ? a.q_norm_w[tid] : 1.f;
   // ---- slot table and per-tile validity masks (one coalesced pass)
   for (int i = tid; i < ((ntiles * AT_TILE + 63) & ~63); i += 512) {
     const int v = v0 + i;
@@ -334,15 +338,13 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
       } else {                                                                               \
         load8(qrow, a.q_t, d0, v);                                                           \
       }                                                                                      \
-      if (a.q_norm_w != nullptr) {                                                           \
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0);                   \
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0 + 4);               \
+      {                                                                                      \
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.qg[d0]);                        \
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.qg[d0 + 4]);                    \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
           v[i] *= inv * g0[i];                                                               \
           v[4 + i] *= inv * g1[i];                                                           \
         }                                                                                    \
-      } else {                                                                               \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) v[i] *= inv;                           \
       }                                                                                      \
       _Pragma("unroll") for (int i = 0; i < 8; i += 2) {                                     \
         const int d = d0 + i;                                                                \
@@ -366,11 +368,17 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   if ((T) < ntiles) {                                                                        \
     const uint8_t* src[8];                                                                   \
     OK = 0u;                                                                                 \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
-      const int id = sm.slot[(T) * AT_TILE + 8 * mw + i];                                    \
-      OK |= (id != -1 ? 1u : 0u) << i;                                                       \
-      src[i] = id >= 0 ? ctx.kv + (int64_t)id * rb                                           \
-                       : (id == -1 ? ctx.kv : ctx.win + (int64_t)(-2 - id) * rb);            \
+    {                                                                                        \
+      const int4* sp4 = reinterpret_cast<const int4*>(&sm.slot[(T) * AT_TILE + 8 * mw]);     \
+      const int4 i0 = sp4[0], i1 = sp4[1];                                                   \
+      const int ids[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};                   \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
+        const int id = ids[i];                                                               \
+        OK |= (id != -1 ? 1u : 0u) << i;                                                     \
+        const bool in_kv = id >= -1;                                                         \
+        const int r = id >= 0 ? id : (id == -1 ? 0 : -2 - id);                               \
+        src[i] = (in_kv ? ctx.kv : ctx.win) + (int64_t)r * rb;                               \
+      }                                                                                      \
     }                                                                                        \
     _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
       if (KVF == CSA_BF16) {                                                                 \
@@ -571,14 +579,20 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
       }
     }
   } else {
-    // partials: O [rows, nsplit, nh, 512] then (m, l) [rows, nsplit, nh, 2]
+    // partials: O / l in bf16 [rows, nsplit, nh, 512], then (m, l) fp32
+    // [rows, nsplit, nh, 2].  Each split's O / l is a convex combination of
+    // its rows, so bf16 costs at most 2^-9 of the largest row value.
     const int64_t rs = (int64_t)row * nsplit + split;
-    float* wo = ws + (rs * a.nh + head) * AT_C;
+    const float il = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    uint16_t* wo = reinterpret_cast<uint16_t*>(ws) + (rs * a.nh + head) * AT_C;
 #pragma unroll
-    for (int nd = 0; nd < 32; ++nd) *reinterpret_cast<f32x4*>(wo + 16 * nd + 4 * g) = O[nd];
+    for (int nd = 0; nd < 32; ++nd)
+      *reinterpret_cast<uint2*>(wo + 16 * nd + 4 * g) =
+          make_uint2(pack_bf16x2(O[nd][0] * il, O[nd][1] * il), pack_bf16x2(O[nd][2] * il, O[nd][3] * il));
     if (g == 0) {
       const int64_t nrows = (int64_t)a.B * a.Tq;
-      float* wml = ws + nrows * nsplit * a.nh * AT_C + (rs * a.nh + head) * 2;
+      float* wml = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(ws) + nrows * nsplit * a.nh * AT_C) +
+                   (rs * a.nh + head) * 2;
       wml[0] = m_run;
       wml[1] = l_tot;
     }
@@ -589,14 +603,16 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
 // one block per (query row, head), one thread per channel pair
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, Rope rt,
                                                              int nsplit,
-                                                             const float* __restrict__ ws) {
+                                                             const void* __restrict__ ws) {
   const int nh = a.nh, c = a.c, d_r = a.rope_dims;
   const int row = blockIdx.x / nh, h = blockIdx.x % nh;
   const int d = 2 * threadIdx.x;
   if (d >= c) return;
   const int64_t nrows = (int64_t)a.B * a.Tq;
-  const float* wml = ws + nrows * nsplit * nh * c + (int64_t)row * nsplit * nh * 2;
-  const float* wo = ws + (int64_t)row * nsplit * nh * c;
+  const uint16_t* wo = reinterpret_cast<const uint16_t*>(ws) + (int64_t)row * nsplit * nh * c;
+  const float* wml = reinterpret_cast<const float*>(reinterpret_cast<const uint16_t*>(ws) +
+                                                    nrows * nsplit * nh * c) +
+                     (int64_t)row * nsplit * nh * 2;
   const float z = a.sink[h];
   float M = z;
 #pragma unroll 8
@@ -604,11 +620,11 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, Rope 
   float den = __expf(z - M), o0 = 0.f, o1 = 0.f;
 #pragma unroll 8
   for (int s = 0; s < nsplit; ++s) {
-    const float e = __expf(wml[((int64_t)s * nh + h) * 2] - M);
-    den = fmaf(wml[((int64_t)s * nh + h) * 2 + 1], e, den);
-    const float2 v = *reinterpret_cast<const float2*>(wo + ((int64_t)s * nh + h) * c + d);
-    o0 = fmaf(v.x, e, o0);
-    o1 = fmaf(v.y, e, o1);
+    const float wgt = wml[((int64_t)s * nh + h) * 2 + 1] * __expf(wml[((int64_t)s * nh + h) * 2] - M);
+    den += wgt;
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(wo + ((int64_t)s * nh + h) * c + d);
+    o0 = fmaf(__uint_as_float(v << 16), wgt, o0);
+    o1 = fmaf(__uint_as_float(v & 0xFFFF0000u), wgt, o1);
   }
   const float inv = 1.0f / den;
   o0 *= inv;
@@ -660,7 +676,7 @@ size_t attend_workspace(const AttendArgs& a) {
   plan_splits(a, &chunk, &nsplit);
   if (nsplit == 1) return 0;
   const size_t rows = (size_t)a.B * a.Tq;
-  return rows * nsplit * a.nh * ((size_t)a.c + 2) * sizeof(float);
+  return rows * nsplit * a.nh * ((size_t)a.c * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s) {
@@ -683,14 +699,14 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s) {
   int chunk, nsplit;
   plan_splits(a, &chunk, &nsplit);
   dim3 grid((unsigned)((int64_t)nsplit * (a.nh / 64) * rows));
-  float* w = (float*)ws;
+  void* w = ws;
   if (a.kv_t == CSA_BF16)
     hipLaunchKernelGGL(attend_mfma_kernel<CSA_BF16>, grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   else
     hipLaunchKernelGGL(attend_mfma_kernel<CSA_FP8MIX>, grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   if (nsplit > 1)
     hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((int64_t)rows * a.nh)),
-                       dim3((a.c / 2 + 63) / 64 * 64), 0, s, a, rt, nsplit, (const float*)w);
+                       dim3((a.c / 2 + 63) / 64 * 64), 0, s, a, rt, nsplit, (const void*)w);
   return hipGetLastError();
 }
 
