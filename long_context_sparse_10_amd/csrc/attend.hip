@@ -216,17 +216,22 @@ __device__ __forceinline__ void load8(const uint8_t* qrow, csa_dtype t, int d, f
   }
 }
 
-// 8 e4m3 codes (two dwords, element order by byte) -> 8 bf16 (exact)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// 8 e4m3 codes (two dwords, element order by byte) -> 8 bf16.  The gfx950
+// conversion decodes OCP e4m3fn (checked against the format's definition on
+// all codes; 0x7F / 0xFF are NaN and never written by the encoders), and an
+// e4m3 value has at most 4 significant bits, so keeping the high half of its
+// fp32 bits is its exact bf16.
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-  u32x4 r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t w = q < 2 ? lo : hi;
-    const int sh = (q & 1) * 16;
-    const float f0 = e4m3_to_f32((w >> sh) & 0xFFu), f1 = e4m3_to_f32((w >> (sh + 8)) & 0xFFu);
-    r[q] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-  }
-  return r;
+  const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+  const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const f32x2 f2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+  const f32x2 f3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  auto hi16 = [](f32x2 f) {
+    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+  };
+  return u32x4{hi16(f0), hi16(f1), hi16(f2), hi16(f3)};
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -380,23 +385,28 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
         src[i] = (in_kv ? ctx.kv : ctx.win) + (int64_t)r * rb;                               \
       }                                                                                      \
     }                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
-      if (KVF == CSA_BF16) {                                                                 \
-        STG[i] = *reinterpret_cast<const u32x4*>(src[i] + 16 * lane);                        \
-      } else if (lane < 56) {                                                                \
-        const uint2 w2 = *reinterpret_cast<const uint2*>(src[i] + 8 * lane);                 \
-        STG[i] = u32x4{w2.x, w2.y, 0u, 0u};                                                  \
-      } else {                                                                               \
-        STG[i] = *reinterpret_cast<const u32x4*>(src[i] + 448 + 16 * (lane - 56));           \
-      }                                                                                      \
-    }                                                                                        \
+    /* bf16 rows: lane l takes bytes 16l..16l+15; FP8 rows (576 B): lanes    */            \
+    /* 0-27 the e4m3 body, 28-35 the bf16 RoPE part, the rest repeat chunk 35 */            \
+    const int ch = KVF == CSA_BF16 ? lane : (lane < 36 ? lane : 35);                         \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                            \
+      STG[i] = *reinterpret_cast<const u32x4*>(src[i] + 16 * ch);                            \
   }
 #define CSA_COMMIT(STG, OK, BUF)                                                             \
   {                                                                                          \
     _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
-      if (KVF == CSA_FP8MIX && lane < 56) STG[i] = e4m3x8_to_bf16(STG[i][0], STG[i][1]);     \
-      if (!((OK >> i) & 1u)) STG[i] = u32x4{0u, 0u, 0u, 0u};                                 \
-      *reinterpret_cast<u32x4*>(&sm.X[BUF][xrow(8 * mw + i)][8 * lane]) = STG[i];           \
+      const bool ok_i = (OK >> i) & 1u;                                                      \
+      uint16_t* xr = &sm.X[BUF][xrow(8 * mw + i)][0];                                       \
+      if (KVF == CSA_BF16) {                                                                 \
+        *reinterpret_cast<u32x4*>(xr + 8 * lane) = ok_i ? STG[i] : u32x4{0u, 0u, 0u, 0u};   \
+      } else if (lane < 28) {                                                                \
+        const u32x4 lo = e4m3x8_to_bf16(STG[i][0], STG[i][1]);                               \
+        const u32x4 hi = e4m3x8_to_bf16(STG[i][2], STG[i][3]);                               \
+        *reinterpret_cast<u32x4*>(xr + 16 * lane) = ok_i ? lo : u32x4{0u, 0u, 0u, 0u};      \
+        *reinterpret_cast<u32x4*>(xr + 16 * lane + 8) = ok_i ? hi : u32x4{0u, 0u, 0u, 0u};  \
+      } else if (lane < 36) {                                                                \
+        *reinterpret_cast<u32x4*>(xr + 448 + 8 * (lane - 28)) =                              \
+            ok_i ? STG[i] : u32x4{0u, 0u, 0u, 0u};                                           \
+      }                                                                                      \
     }                                                                                        \
   }
 
@@ -646,8 +656,10 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, Rope 
 
 // ============================================================ dispatch
 static bool use_mfma(const AttendArgs& a) {
+  // FP8 rows are staged as 448 e4m3 + 64 bf16 bytes: RoPE on the last 64
   return a.c == AT_C && a.nh % 64 == 0 && (a.kv_t == CSA_BF16 || a.kv_t == CSA_FP8MIX) &&
-         (a.q_t == CSA_BF16 || a.q_t == CSA_F32) && a.rope_dims % 2 == 0 && a.rope_dims <= AT_C;
+         (a.q_t == CSA_BF16 || a.q_t == CSA_F32) && a.rope_dims % 2 == 0 && a.rope_dims <= AT_C &&
+         (a.kv_t != CSA_FP8MIX || a.rope_dims == 64);
 }
 
 // slot split: a function of the per-row slot count only (never of the batch
