@@ -303,3 +303,36 @@ def test_attend_deterministic_and_batch_invariant():
     G.decode_attend(g1, idx=it[1:2].contiguous())
     torch.cuda.synchronize()
     assert torch.equal(g1.out[0], a[1])
+
+
+@pytest.mark.parametrize("k,slot", [(32, 5), (4096, 3000)])
+def test_attend_fp8_rows_decode_every_code(k, slot):
+    """FP8/BF16 rows whose e4m3 bodies hold every non-NaN code.  One selected
+    entry, no window and a sink of -1e30: the output is that row exactly, so
+    dims 0..447 must equal the oracle's decode of the codes bit for bit (e4m3
+    values are exact in bf16).  k = 4096 also runs the split / bf16-partial
+    path (one split carries the row, the others are empty)."""
+    d = dev()
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # 254 codes
+    B, N, nh, c, d_r = 2, 8, 64, 512, 64
+    body = np.stack([np.resize(codes, 448), np.resize(codes[::-1], 448)])        # [2, 448]
+    rng = np.random.default_rng(77)
+    rope = F.bf16_encode(rng.standard_normal((B, d_r))).view(np.uint8).reshape(B, 2 * d_r)
+    rows = np.zeros((B, N, 576), np.uint8)
+    rows[:, 2, :448], rows[:, 2, 448:] = body, rope                               # entry 2 carries it
+    kv = torch.from_numpy(rows).to(d)
+    idx = np.full((B, 1, k), -1, np.int32)
+    idx[:, 0, slot] = 2
+    q = torch.from_numpy(I.cast(rng.standard_normal((B, 1, nh, c)).astype(np.float32), "bf16")).to(d).to(torch.bfloat16)
+    q_pos = torch.full((B, 1), 4 * N - 1, dtype=torch.int32, device=d)
+    sink = torch.full((nh,), -1e30, dtype=torch.float32, device=d)
+    win = torch.zeros(B, 1, 576, dtype=torch.uint8, device=d)
+    out = torch.empty(B, 1, nh, c, dtype=torch.bfloat16, device=d)
+    L.sparse_mqa_attend(q, L.BF16, None, 1e-6, d_r, 1e4, q_pos, kv, L.FP8MIX, N,
+                        torch.from_numpy(idx).to(d), k, win, 1, 0, sink, 1 / math.sqrt(c),
+                        B, 1, nh, c, out, L.BF16)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()[:, 0, :, :448]
+    want = F.e4m3_decode(body)                                                    # [2, 448]
+    report("attend fp8 codes", k=k, exact=bool(np.array_equal(got, np.broadcast_to(want[:, None], got.shape))))
+    np.testing.assert_array_equal(got, np.broadcast_to(want[:, None, :], got.shape))
