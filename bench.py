@@ -175,11 +175,19 @@ def run_decode(args, torch, I, G):
         avg[kind] = e0.elapsed_time(e1) * 1e3 / reps
     # the step: one HIP graph per cache copy (captured after the eager warm-up,
     # which also sized every workspace), replayed in rotation
+    side = torch.cuda.Stream()
     graphs = []
     for c in copies:
+        if args.chunks > 1:                      # eager pass sizes the chunk workspaces
+            with torch.cuda.stream(stream):
+                G.decode_step_overlapped(c, [stream, side], args.chunks)
+            torch.cuda.synchronize()
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr, stream=stream):
-            G.decode_step(c, stream)
+            if args.chunks > 1:
+                G.decode_step_overlapped(c, [stream, side], args.chunks)
+            else:
+                G.decode_step(c, stream)
         graphs.append(gr)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
@@ -218,7 +226,8 @@ def run_decode(args, torch, I, G):
                       algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=avg[dom]),
         step=dict(algorithmic_bytes=by["total"] * sp.B, achieved_gbs=step_gbs,
                   frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS, gpu_ms_per_step=gpu_ms / args.steps,
-                  launch="one HIP graph per cache copy",
+                  launch=(f"one HIP graph per cache copy; batch in {args.chunks} groups on 2 streams"
+                          if args.chunks > 1 else "one HIP graph per cache copy"),
                   kernel_us={k: round(v, 2) for k, v in avg.items()}),
     )
     return res, inp
@@ -323,6 +332,8 @@ def main():
     ap.add_argument("--config", default="decode_64k",
                     choices=["decode_64k", "hca_decode_1m", "decode_1m_fp4", "prefill_32k"])
     ap.add_argument("--copies", type=int, default=6, help="cache copies rotated (cold cache)")
+    ap.add_argument("--chunks", type=int, default=1,
+                    help="decode: batch groups whose chains run on two streams (1 = one chain)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")

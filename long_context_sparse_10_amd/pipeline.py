@@ -150,6 +150,56 @@ def decode_step(d: Decode, stream=None):
     decode_attend(d, stream=stream)
 
 
+def _batch_slice(t, b0, b1, B):
+    """Sequences b0..b1-1 of a batch-major tensor (or of a flat per-sequence
+    byte buffer) as a view."""
+    if t is None:
+        return None
+    if t.shape[0] == B:
+        return t[b0:b1]
+    per = t.shape[0] // B
+    return t[b0 * per:b1 * per]
+
+
+def decode_chunks(d: Decode, chunks: int):
+    """The batch cut into ``chunks`` contiguous groups of sequences, each a
+    Decode of views with its own workspaces (made once, kept on ``d``)."""
+    key = ("chunks", chunks)
+    if key not in d.extra:
+        bounds = np.linspace(0, d.B, min(chunks, d.B) + 1).astype(int)
+        subs = []
+        for b0, b1 in zip(bounds[:-1], bounds[1:]):
+            kw = {k: getattr(d, k) for k in d.__dataclass_fields__}
+            for name in ("q", "q_pos", "n_entries", "kv", "win", "qI", "qI_scale", "kI",
+                         "kI_scale", "w", "scores", "idx", "out"):
+                kw[name] = _batch_slice(kw[name], b0, b1, d.B)
+            kw.update(B=int(b1 - b0), ws=None, ws_topk=None, extra={})
+            subs.append(Decode(**kw))
+        d.extra[key] = subs
+    return d.extra[key]
+
+
+def decode_step_overlapped(d: Decode, streams, chunks: int = 2):
+    """The decode step with the batch in ``chunks`` groups whose chains
+    (indexer -> top-k -> attention) run on ``streams`` in rotation, so one
+    group's latency-bound top-k overlaps another group's streaming kernels.
+    ``streams[0]`` is the caller's stream: the others fork from it and join
+    back into it.  Every call is per sequence (the attention split plan never
+    depends on the batch), so the result equals ``decode_step`` bit for bit."""
+    main = streams[0]
+    subs = decode_chunks(d, chunks)
+    fork = torch.cuda.Event()
+    fork.record(main)
+    for s in streams[1:]:
+        s.wait_event(fork)
+    for i, sub in enumerate(subs):
+        decode_step(sub, streams[i % len(streams)])
+    for s in streams[1:]:
+        join = torch.cuda.Event()
+        join.record(s)
+        main.wait_event(join)
+
+
 # ============================================================ prefill
 @dataclass
 class Prefill:
