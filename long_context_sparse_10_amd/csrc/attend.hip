@@ -183,12 +183,15 @@ __device__ __forceinline__ int slot_row_id(const SlotCtx& x, int v) {
   return -2 - (int)(x.win_base + pw % x.win_len);
 }
 
-// Physical LDS row of tile entry e.  With 520-element rows this permutation
-// makes both access patterns below free of bank conflicts (32 banks): the
-// 16-byte S^T operand reads (lane li reads entry 8(li/4) + 4nt + li%4) and the
-// 8-byte transpose reads of the P.V operand (16-lane group g reads entries
-// 8g + 4h + q/4).
-__device__ __forceinline__ int xrow(int e) { return (e & 16) | ((e & 7) << 1) | ((e >> 3) & 1); }
+// Physical LDS row of tile entry e: a bit permutation (e4 -> bit 0, e0 -> 1,
+// e1 -> 2, e3 -> 3, e2 -> 4).  With 520-element rows it keeps both access
+// patterns below free of conflicts on gfx950's 64 LDS banks: the 16-byte S^T
+// operand reads (16 lanes per pass; lane li reads entry 8(li/4) + 4nt + li%4)
+// and the 8-byte transpose reads of the P.V operand (32 lanes per pass; lane q
+// of group g reads entry 8g + 4h + q/4).
+__device__ __forceinline__ int xrow(int e) {
+  return ((e >> 4) & 1) | ((e & 1) << 1) | ((e & 2) << 1) | (e & 8) | ((e & 4) << 2);
+}
 
 struct AttendSmem {
   uint16_t Q[64][AT_LDX];           // normalised, RoPE'd queries of the block's 64 heads
