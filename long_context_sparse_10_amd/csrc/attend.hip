@@ -427,30 +427,26 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
       {                                                                                      \
         const uint16_t* xr0 = &sm.X[BUF][xrow(8 * (li >> 2) + (li & 3))][128 * g];          \
         const uint16_t* xr1 = &sm.X[BUF][xrow(8 * (li >> 2) + 4 + (li & 3))][128 * g];      \
-        const uint16_t* qr = &sm.Q[16 * mw + li][128 * g];                                   \
-        u32x4 ra[4], rb4[4], rq[4];                                                          \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                      \
+        u32x4 ra[3], rb4[3];                                                                 \
+        _Pragma("unroll") for (int q = 0; q < 3; ++q) {                                      \
           ra[q] = *reinterpret_cast<const u32x4*>(xr0 + 8 * q);                              \
           rb4[q] = *reinterpret_cast<const u32x4*>(xr1 + 8 * q);                             \
-          rq[q] = *reinterpret_cast<const u32x4*>(qr + 8 * q);                               \
         }                                                                                    \
         _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                  \
-          const u32x4 a0 = ra[ks & 3], a1 = rb4[ks & 3], bq = rq[ks & 3];                    \
-          if (ks + 4 < 16) {                                                                 \
-            ra[ks & 3] = *reinterpret_cast<const u32x4*>(xr0 + 8 * (ks + 4));                \
-            rb4[ks & 3] = *reinterpret_cast<const u32x4*>(xr1 + 8 * (ks + 4));               \
-            rq[ks & 3] = *reinterpret_cast<const u32x4*>(qr + 8 * (ks + 4));                 \
+          const u32x4 a0 = ra[ks % 3], a1 = rb4[ks % 3];                                     \
+          if (ks + 3 < 16) {                                                                 \
+            ra[ks % 3] = *reinterpret_cast<const u32x4*>(xr0 + 8 * (ks + 3));                \
+            rb4[ks % 3] = *reinterpret_cast<const u32x4*>(xr1 + 8 * (ks + 3));               \
           }                                                                                  \
-          const bf16x8 qb = __builtin_bit_cast(bf16x8, bq);                                  \
-          S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb, S[0], 0, 0, 0); \
-          S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb, S[1], 0, 0, 0); \
+          S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qf[ks], S[0], 0, 0, 0); \
+          S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qf[ks], S[1], 0, 0, 0); \
         }                                                                                    \
-        __builtin_amdgcn_sched_group_barrier(0x100, 12, 1);                                  \
-        _Pragma("unroll") for (int ks = 0; ks < 12; ++ks) {                                  \
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);                                   \
+        _Pragma("unroll") for (int ks = 0; ks < 13; ++ks) {                                  \
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);                                 \
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 1);                                 \
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);                                 \
         }                                                                                    \
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);                                   \
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);                                   \
       }                                                                                      \
       float lg[8];                                                                           \
       float mx = -INFINITY;                                                                  \
@@ -461,12 +457,13 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
         lg[4 * nt + r] = l;                                                                  \
         mx = fmaxf(mx, l);                                                                   \
       }                                                                                      \
-      mx = fmaxf(mx, __shfl_xor(mx, 16));                                                    \
-      mx = fmaxf(mx, __shfl_xor(mx, 32));                                                    \
       /* lazy rescale: the reference maximum moves only when a logit exceeds it */          \
-      /* by more than 8 (weights stay below e^8: safe in fp32 sums and bf16 P) */           \
-      const bool grow = mx > m_run + 8.0f;                                                   \
-      if (__any(grow)) {                                                                     \
+      /* by more than 8 (weights stay below e^8: safe in fp32 sums and bf16 P). */          \
+      /* The max across the head's four lane groups is taken only then. */                  \
+      if (__any(mx > m_run + 8.0f)) {                                                        \
+        mx = fmaxf(mx, __shfl_xor(mx, 16));                                                  \
+        mx = fmaxf(mx, __shfl_xor(mx, 32));                                                  \
+        const bool grow = mx > m_run + 8.0f;                                                 \
         const float m_new = grow ? mx : m_run;                                               \
         const float alpha = __expf(m_run - m_new);                                           \
         l_run *= alpha;                                                                      \
@@ -547,6 +544,11 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   for (int nd = 0; nd < 32; ++nd) O[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
   CSA_QPREP();
   __syncthreads();  // queries and tile 0 in LDS
+  // this wave's query fragments (B operand of S^T), kept in registers
+  bf16x8 qf[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(&sm.Q[16 * mw + li][128 * g + 8 * ks]);
   for (int t = 0; t < ntiles; ++t) {
     CSA_TILE(t, t & 1);
     __syncthreads();
