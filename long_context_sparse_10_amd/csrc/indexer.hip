@@ -200,6 +200,107 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
   }
 }
 
+// ------------------------------------------------------------------ many query rows
+// Prefill shape (bf16, nI 64, cI 128, at least 4 query rows per sequence): one
+// block scores 4 consecutive query rows of a sequence, one wave per row with
+// its query fragments in registers.  The rows share every index key, so keys
+// pass through LDS once per block in 128-entry chunks (double buffered, staged
+// through registers one chunk ahead) and each wave reads them from there.
+// Blocks run from the last (longest) rows backwards.
+constexpr int IR_CH = 128;  // entries per key chunk
+constexpr int IR_LD = 136;  // LDS row stride in bf16 (272 B: 16 rows at one column hit 64 banks)
+
+__global__ __launch_bounds__(256) void indexer_rows_kernel(
+    const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
+    const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int B, int Tq,
+    int Nmax, int m, void* __restrict__ scores, int score_bf16) {
+  __shared__ __attribute__((aligned(16))) uint16_t K[2][IR_CH][IR_LD];
+  const int gps = (Tq + 3) / 4;
+  const int grp = (int)gridDim.x - 1 - (int)blockIdx.x;
+  const int b = grp / gps, r0 = (grp % gps) * 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = lane >> 4, col = lane & 15;
+  const int nent = min(n_entries[b], Nmax);
+  int nv_max = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (r0 + j < Tq) nv_max = max(nv_max, min(nent, (q_pos[b * Tq + r0 + j] + 1) / m));
+  if (nv_max == 0) return;
+  const bool has_row = r0 + wave < Tq;
+  const int row = b * Tq + r0 + (has_row ? wave : 0);
+  const int nv = has_row ? min(nent, (q_pos[row] + 1) / m) : 0;
+
+  bf16x8 afr[4][4];
+  float wr[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t qr = (int64_t)row * 64 + 16 * mt + col;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      afr[mt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qI + qr * 256 + 64 * ks + 16 * kg));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wr[mt][r] = w[(int64_t)row * 64 + 16 * mt + 4 * kg + r];
+  }
+  // chunk staging: thread t moves bytes 16 (t % 16) of entries t / 16 + 16 i
+  const uint8_t* kb = kI + (int64_t)b * Nmax * 256;
+  const int nch = (nv_max + IR_CH - 1) / IR_CH;
+  u32x4 st[8];
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = c * IR_CH + tid / 16 + 16 * i;
+      st[i] = *reinterpret_cast<const u32x4*>(kb + (int64_t)(n < nv_max ? n : 0) * 256 + 16 * (tid % 16));
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(&K[buf][tid / 16 + 16 * i][8 * (tid % 16)]) = st[i];
+  };
+  fetch(0);
+  commit(0);
+  if (nch > 1) fetch(1);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+#pragma unroll 2
+    for (int gi = 0; gi < IR_CH / 16; ++gi) {
+      const int n0 = c * IR_CH + 16 * gi;
+      if (n0 >= nv) break;
+      f32x4 acc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&K[buf][16 * gi + col][32 * ks + 8 * kg]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][ks], bk, acc[mt], 0, 0, 0);
+      }
+      float sc = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], fmaxf(acc[mt][q], 0.f), sc);
+      sc += __shfl_xor(sc, 16);
+      sc += __shfl_xor(sc, 32);
+      const int n = n0 + col;
+      if (kg == 0 && n < nv) {
+        const int64_t o = (int64_t)row * Nmax + n;
+        if (score_bf16)
+          reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(sc);
+        else
+          reinterpret_cast<float*>(scores)[o] = sc;
+      }
+    }
+    if (c + 1 < nch) {
+      commit((c + 1) & 1);
+      if (c + 2 < nch) fetch(c + 2);
+    }
+    __syncthreads();
+  }
+}
+
 hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_t, const float* w,
                           const void* kI, const uint8_t* kI_scale, const int32_t* q_pos,
                           const int32_t* n_entries, int B, int Tq, int nI, int cI, int Nmax,
@@ -207,7 +308,12 @@ hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_
   const int rows = B * Tq;
   if (rows == 0 || Nmax == 0) return hipSuccess;
   const int sbf = score_t == CSA_BF16;
-  if ((in_t == CSA_BF16 || in_t == CSA_MXFP4) && nI == 64 && cI == 128) {
+  if (in_t == CSA_BF16 && nI == 64 && cI == 128 && Tq >= 4) {
+    const int64_t groups = (int64_t)B * ((Tq + 3) / 4);
+    hipLaunchKernelGGL(indexer_rows_kernel, dim3((unsigned)groups), dim3(256), 0, s,
+                       (const uint8_t*)qI, w, (const uint8_t*)kI, q_pos, n_entries, B, Tq, Nmax,
+                       m, scores, sbf);
+  } else if ((in_t == CSA_BF16 || in_t == CSA_MXFP4) && nI == 64 && cI == 128) {
     // about two resident blocks per CU over the whole call; a block covers a
     // multiple of one step of its 4 waves (bf16 128 entries, MXFP4 512)
     const int step = in_t == CSA_MXFP4 ? 512 : 128;

@@ -174,6 +174,43 @@ def test_indexer_mxfp4_matches_quantized_oracle():
         assert np.all(err <= mx_score_bound(inp, b, ref, nv) + 1e-30)
 
 
+@pytest.mark.parametrize("Tq,offset", [(1031, 0), (9, 4093)])
+def test_indexer_bf16_query_rows(Tq, offset):
+    """Many query rows per sequence (the prefill kernel: 4 rows per block share
+    the keys through LDS): two sequences of different lengths, causal
+    positions starting at ``offset``, a ragged last row group; every visible
+    score within the fp32 bound, everything beyond N(q) untouched."""
+    d = dev()
+    rng = np.random.default_rng(Tq + offset)
+    B, nI, cI, m = 2, 64, 128, 4
+    N = (offset + Tq) // m + 3
+    kI = I.cast(rng.standard_normal((B, N, cI)).astype(np.float32), "bf16")
+    qI = I.cast(rng.standard_normal((B, Tq, nI, cI)).astype(np.float32), "bf16")
+    w = rng.standard_normal((B, Tq, nI)).astype(np.float32)
+    q_pos = (offset + np.arange(Tq, dtype=np.int32))[None].repeat(B, 0)
+    n_ent = np.array([N, N - 5], np.int32)
+    scores = torch.full((B, Tq, N), float("nan"), device=d)
+    L.indexer_score(torch.from_numpy(qI).to(d).to(torch.bfloat16), None, L.BF16,
+                    torch.from_numpy(w).to(d), torch.from_numpy(kI).to(d).to(torch.bfloat16), None,
+                    L.BF16, torch.from_numpy(q_pos).to(d), torch.from_numpy(n_ent).to(d), B, Tq,
+                    nI, cI, N, m, scores, L.F32)
+    torch.cuda.synchronize()
+    S = np64(scores)
+    worst = 0.0
+    for b in range(B):
+        for t in list(range(0, Tq, 5)) + [Tq - 1]:
+            nv = int(O.n_visible(int(q_pos[b, t]), m, int(n_ent[b])))
+            want = O.index_scores(qI[b, t].astype(np.float64), w[b, t].astype(np.float64),
+                                  kI[b].astype(np.float64), nv)
+            bound = score_error_bound(qI[b, t].astype(np.float64), w[b, t].astype(np.float64),
+                                      kI[b].astype(np.float64), nv)
+            assert np.all(np.abs(S[b, t, :nv] - want) <= bound + 1e-6), (b, t)
+            assert np.all(np.isnan(S[b, t, nv:])), (b, t)
+            if nv:
+                worst = max(worst, float(np.abs(S[b, t, :nv] - want).max()))
+    report("indexer bf16 query rows", Tq=Tq, max_err=worst)
+
+
 def test_indexer_generic_f32_and_causal_prefill():
     d = dev()
     sp = I.CONFIGS["tiny_csa"]
