@@ -26,6 +26,19 @@
 namespace csa {
 
 constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxima
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy2 = 8.0f * kLog2e;  // 8 nats in log2 units
+
+// 2^x by the hardware instruction (relative error ~1 ulp; -inf -> 0)
+__device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16 (round to nearest even) by v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
 
 struct SlotCtx {
   const uint8_t* kv;
@@ -274,6 +287,7 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   const int g = lane >> 4, li = lane & 15;
   const int head = 64 * hg + 16 * mw + li;  // the head of this lane's softmax state (math)
   const int d_r = a.rope_dims;
+  const float qscale = a.scale * kLog2e;  // queries carry tau * log2 e: logits in log2 units
   const SlotCtx ctx = make_ctx(a, row);
   const int total = ctx.kslots + a.n_win;
   const int v0 = split * chunk;
@@ -365,7 +379,8 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
         }                                                                                    \
       }                                                                                      \
       u32x4 pk;                                                                              \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]); \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
+        pk[i] = pack_bf16x2_hw(v[2 * i] * qscale, v[2 * i + 1] * qscale);                    \
       *reinterpret_cast<u32x4*>(&sm.Q[qhl][d0]) = pk;                                        \
     }                                                                                        \
   }
@@ -448,36 +463,38 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
         }                                                                                    \
         __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);                                   \
       }                                                                                      \
+      /* logits in log2 units (the queries carry tau * log2 e); masked slots -inf */       \
       float lg[8];                                                                           \
-      float mx = -INFINITY;                                                                  \
       _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                       \
-      _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                        \
-        const int e = 8 * g + 4 * nt + r;                                                    \
-        const float l = ((mask >> e) & 1u) ? a.scale * S[nt][r] : -INFINITY;                 \
-        lg[4 * nt + r] = l;                                                                  \
-        mx = fmaxf(mx, l);                                                                   \
+      _Pragma("unroll") for (int r = 0; r < 4; ++r) lg[4 * nt + r] = S[nt][r];               \
+      if (mask != 0xFFFFFFFFu) {                                                             \
+        _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                     \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r)                                        \
+          if (!((mask >> (8 * g + 4 * nt + r)) & 1u)) lg[4 * nt + r] = -INFINITY;            \
       }                                                                                      \
+      float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),                      \
+                       fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));                     \
       /* lazy rescale: the reference maximum moves only when a logit exceeds it */          \
-      /* by more than 8 (weights stay below e^8: safe in fp32 sums and bf16 P). */          \
+      /* by more than 8 nats (weights stay below e^8: safe in fp32 sums and bf16 P). */     \
       /* The max across the head's four lane groups is taken only then. */                  \
-      if (__any(mx > m_run + 8.0f)) {                                                        \
+      if (__any(mx > m_run + kLazy2)) {                                                      \
         mx = fmaxf(mx, __shfl_xor(mx, 16));                                                  \
         mx = fmaxf(mx, __shfl_xor(mx, 32));                                                  \
-        const bool grow = mx > m_run + 8.0f;                                                 \
+        const bool grow = mx > m_run + kLazy2;                                               \
         const float m_new = grow ? mx : m_run;                                               \
-        const float alpha = __expf(m_run - m_new);                                           \
+        const float alpha = exp2f_hw(m_run - m_new);                                         \
         l_run *= alpha;                                                                      \
         m_run = m_new;                                                                       \
         _Pragma("unroll") for (int nd = 0; nd < 32; ++nd) O[nd] *= alpha;                    \
       }                                                                                      \
       float pv[8], ps = 0.f;                                                                 \
       _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
-        pv[i] = __expf(lg[i] - m_run);                                                       \
+        pv[i] = exp2f_hw(lg[i] - m_run);                                                     \
         ps += pv[i];                                                                         \
       }                                                                                      \
       l_run += ps;                                                                           \
       u32x4 pk;                                                                              \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(pv[2 * i], pv[2 * i + 1]); \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2_hw(pv[2 * i], pv[2 * i + 1]); \
       const bf16x8 pf = __builtin_bit_cast(bf16x8, pk); /* P^T: entries 8g..8g+7 of head li */ \
       {                                                                                      \
         /* O^T += X^T P^T, operands by transpose reads, 8 column blocks ahead */            \
@@ -563,10 +580,10 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (nsplit == 1) {
-    const float z = a.sink[head];
+    const float z = a.sink[head] * kLog2e;  // sink in log2 units
     const float M = fmaxf(m_run, z);
-    const float em = __expf(m_run - M);
-    const float f = em / (l_tot * em + __expf(z - M));
+    const float em = exp2f_hw(m_run - M);
+    const float f = em / (l_tot * em + exp2f_hw(z - M));
     uint8_t* orow = (uint8_t*)a.out + ((int64_t)row * a.nh + head) * row_bytes(a.out_t, AT_C, 0);
 #pragma unroll
     for (int nd = 0; nd < 32; ++nd) {
@@ -608,7 +625,7 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
       const int64_t nrows = (int64_t)a.B * a.Tq;
       float* wml = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(ws) + nrows * nsplit * a.nh * AT_C) +
                    (rs * a.nh + head) * 2;
-      wml[0] = m_run;
+      wml[0] = m_run * kLn2;  // natural units for the merge
       wml[1] = l_tot;
     }
   }
