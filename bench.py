@@ -173,33 +173,40 @@ def run_decode(args, torch, I, G):
             e1.record(stream)
         torch.cuda.synchronize()
         avg[kind] = e0.elapsed_time(e1) * 1e3 / reps
-    # the step: one HIP graph per cache copy (captured after the eager warm-up,
-    # which also sized every workspace), replayed in rotation
+    # the step: eager launches (measured faster here than HIP graph replay of
+    # the same calls), or one HIP graph per cache copy with --graph
     side = torch.cuda.Stream()
-    graphs = []
-    for c in copies:
-        if args.chunks > 1:                      # eager pass sizes the chunk workspaces
-            with torch.cuda.stream(stream):
-                G.decode_step_overlapped(c, [stream, side], args.chunks)
-            torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr, stream=stream):
-            if args.chunks > 1:
-                G.decode_step_overlapped(c, [stream, side], args.chunks)
-            else:
-                G.decode_step(c, stream)
-        graphs.append(gr)
+
+    def step_fn(c):
+        if args.chunks > 1:
+            G.decode_step_overlapped(c, [stream, side], args.chunks)
+        else:
+            G.decode_step(c, stream)
+    with torch.cuda.stream(stream):
+        for c in copies:                         # sizes the chunk workspaces
+            step_fn(c)
     torch.cuda.synchronize()
+    if args.graph:
+        graphs = []
+        for c in copies:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                step_fn(c)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        run_step = lambda i: graphs[i % len(graphs)].replay()
+    else:
+        run_step = lambda i: step_fn(copies[i % len(copies)])
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
+            run_step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
     with torch.cuda.stream(stream):
         e0.record(stream)
         for i in range(args.steps):
-            graphs[i % len(graphs)].replay()
+            run_step(i)
         e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
@@ -226,8 +233,8 @@ def run_decode(args, torch, I, G):
                       algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=avg[dom]),
         step=dict(algorithmic_bytes=by["total"] * sp.B, achieved_gbs=step_gbs,
                   frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS, gpu_ms_per_step=gpu_ms / args.steps,
-                  launch=(f"one HIP graph per cache copy; batch in {args.chunks} groups on 2 streams"
-                          if args.chunks > 1 else "one HIP graph per cache copy"),
+                  launch=("HIP graph per cache copy" if args.graph else "eager launches")
+                  + (f"; batch in {args.chunks} groups on 2 streams" if args.chunks > 1 else ""),
                   kernel_us={k: round(v, 2) for k, v in avg.items()}),
     )
     return res, inp
@@ -332,6 +339,7 @@ def main():
     ap.add_argument("--config", default="decode_64k",
                     choices=["decode_64k", "hca_decode_1m", "decode_1m_fp4", "prefill_32k"])
     ap.add_argument("--copies", type=int, default=6, help="cache copies rotated (cold cache)")
+    ap.add_argument("--graph", action="store_true", help="decode: replay each step as a HIP graph")
     ap.add_argument("--chunks", type=int, default=1,
                     help="decode: batch groups whose chains run on two streams (1 = one chain)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -8,9 +8,10 @@
 // lower index, and rows with fewer than k visible entries are padded with -1.
 //
 // Rows of up to 16 * 1024 entries run in one block per row with the keys in
-// registers: thread t owns the contiguous entries [16 t, 16 t + 16), every
-// radix pass works on registers, and the ordered compaction needs a single
-// block-wide scan.  Longer rows (few decode rows over 2^18 entries) spread over
+// registers: thread t owns the contiguous entries [16 t, 16 t + 16).  The
+// first digit is counted block-wide; the keys sharing it with the k-th largest
+// (the candidates) are compacted into LDS and one wave resolves the remaining
+// digits over them alone; the ordered compaction is a single block-wide scan.  Longer rows (few decode rows over 2^18 entries) spread over
 // many blocks per row: per-block digit histograms, a per-row reduction that
 // fixes the digit, and after the last digit per-block counts and an ordered
 // emit at each block's offset.
@@ -122,6 +123,19 @@ __device__ __forceinline__ void find_digit(const int* hist, int nbins, int remai
   }
 }
 
+// exclusive prefix of one int per lane within the wave; *total gets the wave sum
+__device__ __forceinline__ int wave_scan_excl(int v, int* total) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(x, o);
+    if (lane >= o) x += t;
+  }
+  *total = __shfl(x, 63);
+  return x - v;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ scores,
                                                     const int32_t* __restrict__ q_pos,
@@ -129,11 +143,12 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
                                                     int Nmax, int m, int k, int vec,
                                                     int32_t* __restrict__ idx) {
   __shared__ int hist[2048];
+  extern __shared__ uint32_t cand[];  // [16 * blockDim]: keys sharing the k-th's first digit
   __shared__ int scan_ws[16];
   __shared__ uint32_t sh_digit;
-  __shared__ int sh_above;
+  __shared__ int sh_above, sh_ncand;
   const int row = blockIdx.x, b = row / Tq;
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
   const int nv = min(min(n_entries[b], Nmax), (q_pos[row] + 1) / m);
   int32_t* out = idx + (int64_t)row * k;
   const void* srow = BF16 ? (const void*)((const uint16_t*)scores + (int64_t)row * Nmax)
@@ -151,29 +166,68 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
 #pragma unroll
     for (int i = 0; i < 16; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
   }
-  // ---- radix select: digits of 11/11/10 bits (fp32 keys) or 8/8 bits (bf16 keys)
-  uint32_t prefix = 0u, pmask = 0u;
-  int remaining = k;  // rank still to locate inside the current prefix class
-  int shift = BF16 ? 16 : 32;
-  while (shift > 0) {
-    const int width = BF16 ? 8 : (shift == 32 || shift == 21 ? 11 : 10);
-    shift -= width;
-    const int nbins = 1 << width;
-    const uint32_t dmask = (uint32_t)nbins - 1u;
-    for (int i = tid; i < nbins; i += nt) hist[i] = 0;
-    __syncthreads();
+  // ---- first digit, block-wide: 11 bits of fp32 keys (bits 31..21), 8 of bf16 (15..8)
+  constexpr int SH1 = BF16 ? 8 : 21;
+  constexpr int NB1 = 1 << (BF16 ? 8 : 11);
+  for (int i = tid; i < NB1; i += nt) hist[i] = 0;
+  if (tid == 0) sh_ncand = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (s0 + i < nv) atomicAdd(&hist[key[i] >> SH1], 1);
+  __syncthreads();
+  find_digit(hist, NB1, k, &sh_digit, &sh_above);
+  __syncthreads();
+  const uint32_t d1 = sh_digit;
+  int remaining = k - sh_above;  // rank to locate among the keys of digit d1
+  // ---- candidates: keys of digit d1, appended to LDS (one atomic per wave)
+  {
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mine += (s0 + i < nv && (key[i] >> SH1) == d1) ? 1 : 0;
+    int wtot;
+    int pos = wave_scan_excl(mine, &wtot);
+    int base = 0;
+    if (lane == 0 && wtot) base = atomicAdd(&sh_ncand, wtot);
+    pos += __shfl(base, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (s0 + i < nv && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
-    __syncthreads();
-    find_digit(hist, nbins, remaining, &sh_digit, &sh_above);
-    __syncthreads();
-    remaining -= sh_above;
-    prefix |= sh_digit << shift;
-    pmask |= dmask << shift;
+      if (s0 + i < nv && (key[i] >> SH1) == d1) cand[pos++] = key[i];
   }
-  const uint32_t kstar = prefix;
-  const int need_eq = remaining;  // entries equal to K* to take, lowest index first
+  __syncthreads();
+  // ---- remaining digits over the candidates by wave 0 alone (no block barriers):
+  // fp32 keys 11 + 10 bits (20..10, 9..0), bf16 keys 8 bits (7..0)
+  if (tid < 64) {
+    const int nc = sh_ncand;
+    uint32_t prefix = d1 << SH1, pmask = ~0u << SH1;
+    int shift = SH1;
+    while (shift > 0) {
+      const int width = BF16 ? 8 : (shift == 21 ? 11 : 10);
+      shift -= width;
+      const int nbins = 1 << width;
+      const uint32_t dmask = (uint32_t)nbins - 1u;
+      for (int i = lane; i < nbins; i += 64) hist[i] = 0;
+      __builtin_amdgcn_wave_barrier();
+      for (int i = lane; i < nc; i += 64) {
+        const uint32_t kk = cand[i];
+        if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & dmask], 1);
+      }
+      __builtin_amdgcn_wave_barrier();
+      find_digit(hist, nbins, remaining, &sh_digit, &sh_above);
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t dg = __shfl(sh_digit, 0);
+      remaining -= __shfl(sh_above, 0);
+      prefix |= dg << shift;
+      pmask |= dmask << shift;
+    }
+    if (lane == 0) {
+      sh_digit = prefix;
+      sh_above = remaining;
+    }
+  }
+  __syncthreads();
+  const uint32_t kstar = sh_digit;
+  const int need_eq = sh_above;  // entries equal to K* to take, lowest index first
   // ---- ordered compaction: one block-wide scan of (above, equal) counts
   int gt = 0, eq = 0;
 #pragma unroll
@@ -457,12 +511,13 @@ hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_p
   }
   // one block per row, 16 keys per thread (counts stay below 2^16 for the packed scan)
   const int threads = Nmax > 4096 ? 1024 : (Nmax > 1024 ? 256 : 64);
+  const size_t cand_bytes = (size_t)16 * threads * sizeof(uint32_t);
   if (bf)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(threads), 0, s, scores, q_pos,
-                       n_entries, Tq, Nmax, m, k, vec, idx);
+    hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(threads), cand_bytes, s, scores,
+                       q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(rows), dim3(threads), 0, s, scores, q_pos,
-                       n_entries, Tq, Nmax, m, k, vec, idx);
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(rows), dim3(threads), cand_bytes, s, scores,
+                       q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
   return hipGetLastError();
 }
 
