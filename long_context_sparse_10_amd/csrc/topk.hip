@@ -123,6 +123,32 @@ __device__ __forceinline__ void find_digit(const int* hist, int nbins, int remai
   }
 }
 
+// Block-wide version of find_digit for large histograms: thread t owns the
+// nbins / blockDim digits just below those of thread t-1 (descending), one
+// block scan orders the ranges, and the thread whose range holds the rank
+// scans it.  Every thread of the block must call.
+__device__ __forceinline__ void find_digit_block(const int* hist, int nbins, int remaining,
+                                                 int* scan_ws, uint32_t* digit, int* above) {
+  const int per = nbins / blockDim.x;
+  const int top = nbins - 1 - per * threadIdx.x;
+  int cnt = 0;
+  for (int i = 0; i < per; ++i) cnt += hist[top - i];
+  int total;
+  const int excl = block_scan_excl(cnt, scan_ws, &total);
+  if (excl < remaining && excl + cnt >= remaining) {
+    int acc = excl;
+    for (int i = 0; i < per; ++i) {
+      const int h = hist[top - i];
+      if (acc + h >= remaining) {
+        *digit = (uint32_t)(top - i);
+        *above = acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+}
+
 // exclusive prefix of one int per lane within the wave; *total gets the wave sum
 __device__ __forceinline__ int wave_scan_excl(int v, int* total) {
   const int lane = threadIdx.x & 63;
@@ -142,7 +168,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
                                                     const int32_t* __restrict__ n_entries, int Tq,
                                                     int Nmax, int m, int k, int vec,
                                                     int32_t* __restrict__ idx) {
-  __shared__ int hist[2048];
+  __shared__ int hist[8192];
   extern __shared__ uint32_t cand[];  // [16 * blockDim]: keys sharing the k-th's first digit
   __shared__ int scan_ws[16];
   __shared__ uint32_t sh_digit;
@@ -166,9 +192,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
 #pragma unroll
     for (int i = 0; i < 16; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
   }
-  // ---- first digit, block-wide: 11 bits of fp32 keys (bits 31..21), 8 of bf16 (15..8)
-  constexpr int SH1 = BF16 ? 8 : 21;
-  constexpr int NB1 = 1 << (BF16 ? 8 : 11);
+  // ---- first digit, block-wide: 13 bits of fp32 keys (bits 31..19), 10 of bf16
+  // (15..6); wide digits spread the clustered score exponents over many bins
+  constexpr int SH1 = BF16 ? 6 : 19;
+  constexpr int NB1 = 1 << (BF16 ? 10 : 13);
   for (int i = tid; i < NB1; i += nt) hist[i] = 0;
   if (tid == 0) sh_ncand = 0;
   __syncthreads();
@@ -176,7 +203,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
   for (int i = 0; i < 16; ++i)
     if (s0 + i < nv) atomicAdd(&hist[key[i] >> SH1], 1);
   __syncthreads();
-  find_digit(hist, NB1, k, &sh_digit, &sh_above);
+  find_digit_block(hist, NB1, k, scan_ws, &sh_digit, &sh_above);
   __syncthreads();
   const uint32_t d1 = sh_digit;
   int remaining = k - sh_above;  // rank to locate among the keys of digit d1
@@ -196,13 +223,13 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
   }
   __syncthreads();
   // ---- remaining digits over the candidates by wave 0 alone (no block barriers):
-  // fp32 keys 11 + 10 bits (20..10, 9..0), bf16 keys 8 bits (7..0)
+  // fp32 keys 10 + 9 bits (18..9, 8..0), bf16 keys 6 bits (5..0)
   if (tid < 64) {
     const int nc = sh_ncand;
     uint32_t prefix = d1 << SH1, pmask = ~0u << SH1;
     int shift = SH1;
     while (shift > 0) {
-      const int width = BF16 ? 8 : (shift == 21 ? 11 : 10);
+      const int width = BF16 ? 6 : (shift == 19 ? 10 : 9);
       shift -= width;
       const int nbins = 1 << width;
       const uint32_t dmask = (uint32_t)nbins - 1u;
@@ -510,7 +537,8 @@ hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_p
     return hipGetLastError();
   }
   // one block per row, 16 keys per thread (counts stay below 2^16 for the packed scan)
-  const int threads = Nmax > 4096 ? 1024 : (Nmax > 1024 ? 256 : 64);
+  int threads = 64;  // the smallest power of two >= Nmax / 16, at least one wave
+  while (threads * 16 < Nmax) threads *= 2;
   const size_t cand_bytes = (size_t)16 * threads * sizeof(uint32_t);
   if (bf)
     hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(threads), cand_bytes, s, scores,
