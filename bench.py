@@ -40,14 +40,14 @@ METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP
 # of known size (--copy-probe).  An entry holds for the kernel source it was
 # taken on (sha256 of the .hip file); after any change it reports null.
 TRAFFIC = {
-    "decode_64k": dict(src="indexer.hip", sha256="95037799299b7ce7a02c010d03c983d2cb90de83799586718bc8b5f4a7419817",
-                fetch_kib=67664.5, write_kib=2048.5, fetch_scale=1.9998, write_scale=1.0),
-    "hca_decode_1m": dict(src="attend.hip", sha256="657d8f191ce02f313b6f8777d29aaf8cfecc35944588d12f263159a3950e66cf",
-                fetch_kib=70997.8, write_kib=32896.0, fetch_scale=1.9998, write_scale=1.0),
-    "decode_1m_fp4": dict(src="indexer.hip", sha256="95037799299b7ce7a02c010d03c983d2cb90de83799586718bc8b5f4a7419817",
-                fetch_kib=69898.2, write_kib=4096.5, fetch_scale=1.9998, write_scale=1.0),
-    "prefill_32k": dict(src="attend.hip", sha256="657d8f191ce02f313b6f8777d29aaf8cfecc35944588d12f263159a3950e66cf",
-                fetch_kib=3295163.5, write_kib=2097207.2, fetch_scale=1.9998, write_scale=1.0),
+    "decode_64k": dict(src="indexer.hip", sha256="cf0bb6345b2835efd0cb8312177db31e9c68837b777a8ebb0c8ad990dea3ba19",
+                fetch_kib=67667.0, write_kib=2048.4, fetch_scale=1.9998, write_scale=1.0),
+    "hca_decode_1m": dict(src="attend.hip", sha256="5b4d4b06a72f3d4197e2e30bced149a626c0df3d59d0b90bcc580457e96529c4",
+                fetch_kib=80743.0, write_kib=18560.3, fetch_scale=1.9998, write_scale=1.0),
+    "decode_1m_fp4": dict(src="indexer.hip", sha256="cf0bb6345b2835efd0cb8312177db31e9c68837b777a8ebb0c8ad990dea3ba19",
+                fetch_kib=69890.2, write_kib=4096.8, fetch_scale=1.9998, write_scale=1.0),
+    "prefill_32k": dict(src="attend.hip", sha256="5b4d4b06a72f3d4197e2e30bced149a626c0df3d59d0b90bcc580457e96529c4",
+                fetch_kib=3600826.6, write_kib=2222392.2, fetch_scale=1.9998, write_scale=1.0),
 }
 
 
