@@ -174,9 +174,9 @@ def test_indexer_mxfp4_matches_quantized_oracle():
         assert np.all(err <= mx_score_bound(inp, b, ref, nv) + 1e-30)
 
 
-@pytest.mark.parametrize("Tq,offset", [(1031, 0), (9, 4093)])
+@pytest.mark.parametrize("Tq,offset", [(1031, 0), (37, 4093), (9, 4093)])
 def test_indexer_bf16_query_rows(Tq, offset):
-    """Many query rows per sequence (the prefill kernel: 4 rows per block share
+    """Many query rows per sequence (the prefill kernel: a block of rows shares
     the keys through LDS): two sequences of different lengths, causal
     positions starting at ``offset``, a ragged last row group; every visible
     score within the fp32 bound, everything beyond N(q) untouched."""
