@@ -264,6 +264,7 @@ def run_prefill(args, torch, I, G):
             G.prefill_attention_path(p, stream)
     torch.cuda.synchronize()
     import long_context_sparse_10_amd as L
+    sfmt = L.BF16 if sp.index_format == "mxfp4" else L.F32
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_start = time.perf_counter()
     scale = 1.0 / math.sqrt(sp.c)
@@ -271,10 +272,9 @@ def run_prefill(args, torch, I, G):
         for i in range(args.steps):
             e = ev[i]
             e[0].record(stream)
-            L.indexer_score(p.qI, None, L.BF16, p.w, p.kI, None, L.BF16, p.q_pos, p.n_entries, 1,
-                            sp.T, sp.nI, sp.cI, n, sp.m, p.scores, L.F32, stream)
+            G.prefill_indexer(p, stream)
             e[1].record(stream)
-            L.topk_select(p.scores, L.F32, p.q_pos, p.n_entries, 1, sp.T, n, sp.m, sp.k, p.idx,
+            L.topk_select(p.scores, sfmt, p.q_pos, p.n_entries, 1, sp.T, n, sp.m, sp.k, p.idx,
                           None, stream)
             e[2].record(stream)
             L.sparse_mqa_attend(p.q, L.BF16, p.gamma, 1e-6, sp.d_r, 1e4, p.q_pos, p.kv, L.BF16, n,
@@ -292,9 +292,10 @@ def run_prefill(args, torch, I, G):
     res = dict(
         metric=METRIC, value=tflops, unit="TFLOP/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak",
-        vs_baseline=None, dtype="bf16", data="synthetic",
+        vs_baseline=None, dtype="bf16" if sp.index_format == "bf16" else "bf16+mxfp4 indexer",
+        data="synthetic",
         config=dict(workload=sp.name, seq_len=sp.T, hidden=sp.d, heads=sp.nh, head_dim=sp.c,
-                    top_k=sp.k, indexer=f"{sp.nI}x{sp.cI}", window=sp.n_win),
+                    top_k=sp.k, indexer=f"{sp.nI}x{sp.cI} {sp.index_format}", window=sp.n_win),
         roofline=dict(bound="mfma", kernel="attend", achieved=att, peak=BF16_PEAK_TFLOPS,
                       unit="TFLOP/s", frac=att / BF16_PEAK_TFLOPS, traffic=None,
                       algorithmic_flops_per_launch=fa, avg_launch_us=avg["attend"]),
@@ -337,7 +338,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_64k",
-                    choices=["decode_64k", "hca_decode_1m", "decode_1m_fp4", "prefill_32k"])
+                    choices=["decode_64k", "hca_decode_1m", "decode_1m_fp4", "prefill_32k",
+                             "prefill_32k_mxfp4"])
     ap.add_argument("--copies", type=int, default=6, help="cache copies rotated (cold cache)")
     ap.add_argument("--graph", action="store_true", help="decode: replay each step as a HIP graph")
     ap.add_argument("--chunks", type=int, default=1,
@@ -357,14 +359,14 @@ def main():
         return
     import csa_inputs as I
     from long_context_sparse_10_amd import pipeline as G
-    if args.config == "prefill_32k":
+    if args.config.startswith("prefill"):
         args.copies = 1
         res, inp = run_prefill(args, torch, I, G)
     else:
         res, inp = run_decode(args, torch, I, G)
     res["roofline"]["traffic"] = kernel_traffic(args.config)
     if not args.no_cpu_baseline:
-        if args.config == "prefill_32k":
+        if args.config.startswith("prefill"):
             rows = np.linspace(0, inp["T"] - 1, 64).astype(int)
             res["cpu_baseline"] = cpu_baseline_prefill(inp, rows)
         else:

@@ -16,6 +16,7 @@ synthetic inputs stand in):
   (RoPE 64), 64 query heads, indexer 64 x 128 bf16, top-k 1024.
 * prefill_32k -- one sequence of 32,768 tokens, hidden 4096 bf16, compressor
   weights ~ N(0, 1/4096), 64 heads x 512, indexer 64 x 128, top-k 1024.
+  prefill_32k_mxfp4 is the same prefill with MXFP4 index keys and queries.
 * hca_decode_1m -- 16 sequences x 1,048,576 tokens, m' = 128 (8,192 entries),
   bf16 KV, 64 heads.
 * decode_1m_fp4 -- 8 sequences x 1,048,576 tokens (262,144 entries), 128
@@ -79,6 +80,10 @@ CONFIGS = {
                        cI=128, k=1024, seed=1002),
     "prefill_32k": Spec("prefill_32k", "prefill", m=4, c=512, d_r=64, nh=64, T=32768, d=4096,
                         nI=64, cI=128, k=1024, seed=1003),
+    # the prefill with MXFP4 index keys and queries (bf16 scores): the same
+    # seeded inputs, only the indexer's storage format differs
+    "prefill_32k_mxfp4": Spec("prefill_32k_mxfp4", "prefill", m=4, c=512, d_r=64, nh=64, T=32768,
+                              d=4096, nI=64, cI=128, k=1024, index_format="mxfp4", seed=1003),
     "hca_decode_1m": Spec("hca_decode_1m", "hca_decode", m=128, c=512, d_r=64, nh=64, B=16,
                           L=1 << 20, seed=1004),
     "decode_1m_fp4": Spec("decode_1m_fp4", "decode", m=4, c=512, d_r=64, nh=128, B=8,

@@ -305,6 +305,111 @@ __global__ __launch_bounds__(64 * R) void indexer_rows_kernel(
   }
 }
 
+// MXFP4 form of indexer_rows_kernel: 256-entry chunks of E2M1 codes (80-byte
+// LDS rows, conflict-free for 16 lanes at one column) plus their e8m0 scale
+// dwords; each 16-entry group is 4 block-scaled fp4 MFMAs (one per head tile).
+constexpr int IRX_CH = 256;  // entries per key chunk
+constexpr int IRX_LD = 80;   // LDS bytes per staged row (64 bytes of codes)
+
+template <int R>
+__global__ __launch_bounds__(64 * R) void indexer_rows_mx_kernel(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ kI,
+    const uint8_t* __restrict__ kI_scale, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int B, int Tq, int Nmax, int m,
+    void* __restrict__ scores, int score_bf16) {
+  static_assert(64 * R == 4 * IRX_CH, "one 16-byte piece of codes per thread per chunk");
+  __shared__ __attribute__((aligned(16))) uint8_t Kc[2][IRX_CH][IRX_LD];
+  __shared__ uint32_t Ks[2][IRX_CH];
+  const int gps = (Tq + R - 1) / R;
+  const int grp = (int)gridDim.x - 1 - (int)blockIdx.x;
+  const int b = grp / gps, r0 = (grp % gps) * R;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kg = lane >> 4, col = lane & 15;
+  const int nent = min(n_entries[b], Nmax);
+  int nv_max = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    if (r0 + j < Tq) nv_max = max(nv_max, min(nent, (q_pos[b * Tq + r0 + j] + 1) / m));
+  if (nv_max == 0) return;
+  const bool has_row = r0 + wave < Tq;
+  const int row = b * Tq + r0 + (has_row ? wave : 0);
+  const int nv = has_row ? min(nent, (q_pos[row] + 1) / m) : 0;
+
+  // query fragments of head 16 mt + col: codes of dims 32 kg .. 32 kg + 31 and
+  // their scale (in byte 0)
+  u32x4 aq[4];
+  int asc[4];
+  float wr[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t qr = (int64_t)row * 64 + 16 * mt + col;
+    aq[mt] = *reinterpret_cast<const u32x4*>(qI + qr * 64 + 16 * kg);
+    asc[mt] = (int)(*reinterpret_cast<const uint32_t*>(qI_scale + qr * 4) >> (8 * kg));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wr[mt][r] = w[(int64_t)row * 64 + 16 * mt + 4 * kg + r];
+  }
+  // staging: thread t moves code bytes 16 (t % 4) of entry t / 4; threads below
+  // IRX_CH also move entry t's scale dword
+  const uint8_t* kb = kI + (int64_t)b * Nmax * 64;
+  const uint32_t* ksb = reinterpret_cast<const uint32_t*>(kI_scale) + (int64_t)b * Nmax;
+  const int nch = (nv_max + IRX_CH - 1) / IRX_CH;
+  u32x4 st;
+  uint32_t ss = 0u;
+  auto fetch = [&](int c) {
+    const int n = c * IRX_CH + tid / 4;
+    st = *reinterpret_cast<const u32x4*>(kb + (int64_t)(n < nv_max ? n : 0) * 64 + 16 * (tid % 4));
+    if (tid < IRX_CH) {
+      const int ns = c * IRX_CH + tid;
+      ss = ksb[ns < nv_max ? ns : 0];
+    }
+  };
+  auto commit = [&](int buf) {
+    *reinterpret_cast<u32x4*>(&Kc[buf][tid / 4][16 * (tid % 4)]) = st;
+    if (tid < IRX_CH) Ks[buf][tid] = ss;
+  };
+  fetch(0);
+  commit(0);
+  if (nch > 1) fetch(1);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+#pragma unroll 2
+    for (int gi = 0; gi < IRX_CH / 16; ++gi) {
+      const int n0 = c * IRX_CH + 16 * gi;
+      if (n0 >= nv) break;
+      const i32x8 bk = widen(*reinterpret_cast<const u32x4*>(&Kc[buf][16 * gi + col][16 * kg]));
+      const int bs = (int)(Ks[buf][16 * gi + col] >> (8 * kg));
+      f32x4 acc[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(aq[mt]), bk,
+                                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4,
+                                                                   0, asc[mt], 0, bs);
+      float sc = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], fmaxf(acc[mt][q], 0.f), sc);
+      sc += __shfl_xor(sc, 16);
+      sc += __shfl_xor(sc, 32);
+      const int n = n0 + col;
+      if (kg == 0 && n < nv) {
+        const int64_t o = (int64_t)row * Nmax + n;
+        if (score_bf16)
+          reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(sc);
+        else
+          reinterpret_cast<float*>(scores)[o] = sc;
+      }
+    }
+    if (c + 1 < nch) {
+      commit((c + 1) & 1);
+      if (c + 2 < nch) fetch(c + 2);
+    }
+    __syncthreads();
+  }
+}
+
 hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_t, const float* w,
                           const void* kI, const uint8_t* kI_scale, const int32_t* q_pos,
                           const int32_t* n_entries, int B, int Tq, int nI, int cI, int Nmax,
@@ -317,6 +422,12 @@ hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_
     hipLaunchKernelGGL(indexer_rows_kernel<IR_ROWS>, dim3((unsigned)groups), dim3(64 * IR_ROWS), 0,
                        s, (const uint8_t*)qI, w, (const uint8_t*)kI, q_pos, n_entries, B, Tq,
                        Nmax, m, scores, sbf);
+  } else if (in_t == CSA_MXFP4 && nI == 64 && cI == 128 && Tq >= IR_ROWS) {
+    const int64_t groups = (int64_t)B * ((Tq + IR_ROWS - 1) / IR_ROWS);
+    hipLaunchKernelGGL(indexer_rows_mx_kernel<IR_ROWS>, dim3((unsigned)groups),
+                       dim3(64 * IR_ROWS), 0, s, (const uint8_t*)qI, qI_scale, w,
+                       (const uint8_t*)kI, kI_scale, q_pos, n_entries, B, Tq, Nmax, m, scores,
+                       sbf);
   } else if ((in_t == CSA_BF16 || in_t == CSA_MXFP4) && nI == 64 && cI == 128) {
     // about two resident blocks per CU over the whole call; a block covers a
     // multiple of one step of its 4 waves (bf16 128 entries, MXFP4 512)

@@ -217,6 +217,8 @@ class Prefill:
     gamma: torch.Tensor
     kv: Optional[torch.Tensor] = None
     kI: Optional[torch.Tensor] = None
+    kI_scale: Optional[torch.Tensor] = None
+    qI_scale: Optional[torch.Tensor] = None
     win: Optional[torch.Tensor] = None
     scores: Optional[torch.Tensor] = None
     idx: Optional[torch.Tensor] = None
@@ -240,6 +242,9 @@ def upload_prefill(inp: dict, device="cuda") -> Prefill:
                 n_entries=torch.tensor([T // sp.m], dtype=torch.int32, device=device),
                 sink=torch.from_numpy(inp["sink"]).to(device),
                 gamma=torch.ones(sp.c, dtype=torch.float32, device=device))
+    if sp.nI and sp.index_format == "mxfp4":
+        # MXFP4 index queries, encoded by the library from the bf16 values
+        p.qI, p.qI_scale = encode_rows(p.qI.float(), C.MXFP4, T * sp.nI, sp.cI)
     return p
 
 
@@ -260,13 +265,25 @@ def prefill_compress(p: Prefill, stream=None):
     if sp.nI:
         ifmt = FMT[sp.index_format]
         p.kI = torch.empty(max(n, 1) * _row_bytes(ifmt, sp.cI, 0), dtype=torch.uint8, device=dev)
+        if ifmt == C.MXFP4:
+            p.kI_scale = torch.empty(max(n, 1) * (sp.cI // 32), dtype=torch.uint8, device=dev)
         p.ws = C.csa_compress(p.H, p.dt, 1, T, sp.d, W["WI_kv_a"], W["WI_z_a"], W["WI_kv_b"],
                               W["WI_z_b"], W["biasI_a"], W["biasI_b"], sp.m, 1, sp.cI, None, EPS, 0,
-                              ROPE_THETA, sp.m, 0, p.kI, None, ifmt, p.ws, stream)
+                              ROPE_THETA, sp.m, 0, p.kI, p.kI_scale, ifmt, p.ws, stream)
     p.win = torch.empty(T * _row_bytes(kv_fmt, sp.c, sp.d_r), dtype=torch.uint8, device=dev)
     p.ws = C.csa_compress(p.H, p.dt, 1, T, sp.d, W["W_win"], None, None, None, None, None, 1, 0,
                           sp.c, p.gamma, EPS, sp.d_r, ROPE_THETA, 1, 0, p.win, None, kv_fmt, p.ws,
                           stream)
+
+
+def prefill_indexer(p: Prefill, stream=None):
+    """Causal indexer scores of every query row of the prefill."""
+    sp = p.spec
+    ifmt = FMT[sp.index_format]
+    sfmt = C.BF16 if ifmt == C.MXFP4 else C.F32
+    C.indexer_score(p.qI, p.qI_scale, ifmt, p.w, p.kI, p.kI_scale, ifmt, p.q_pos, p.n_entries, 1,
+                    p.q_pos.numel(), sp.nI, sp.cI, max(p.T // sp.m, 1), sp.m, p.scores, sfmt,
+                    stream)
 
 
 def prefill_attention_path(p: Prefill, stream=None):
@@ -282,12 +299,13 @@ def prefill_attention_path(p: Prefill, stream=None):
     kv_fmt = FMT[sp.kv_format]
     if sp.nI:
         ifmt = FMT[sp.index_format]
+        sfmt = C.BF16 if ifmt == C.MXFP4 else C.F32   # MXFP4 indexer: bf16 scores
         if p.scores is None:
-            p.scores = torch.empty(1, Tq, n, dtype=torch.float32, device=dev)
+            sdt = torch.bfloat16 if sfmt == C.BF16 else torch.float32
+            p.scores = torch.empty(1, Tq, n, dtype=sdt, device=dev)
             p.idx = torch.empty(1, Tq, sp.k, dtype=torch.int32, device=dev)
-        C.indexer_score(p.qI, None, ifmt, p.w, p.kI, None, ifmt, p.q_pos, p.n_entries, 1, Tq, sp.nI,
-                        sp.cI, n, sp.m, p.scores, C.F32, stream)
-        C.topk_select(p.scores, C.F32, p.q_pos, p.n_entries, 1, Tq, n, sp.m, sp.k, p.idx, None,
+        prefill_indexer(p, stream)
+        C.topk_select(p.scores, sfmt, p.q_pos, p.n_entries, 1, Tq, n, sp.m, sp.k, p.idx, None,
                       stream)
         p.ws_attend = C.sparse_mqa_attend(p.q, ot, p.gamma, EPS, sp.d_r, ROPE_THETA, p.q_pos, p.kv,
                                           kv_fmt, n, p.idx, sp.k, p.win, T, sp.n_win, p.sink, scale,

@@ -106,7 +106,7 @@ def prefill_caches(inp):
         kI = O.compress(H, inp["WI_kv_a"], inp["WI_z_a"], inp["biasI_a"], sp.m, inp["WI_kv_b"],
                         inp["WI_z_b"], inp["biasI_b"], normalize=False)
         out["kI_exact"] = kI
-        out["kI"] = store(kI, sp.index_format, 0)
+        out["kI"] = mxfp4_values(kI)[0] if sp.index_format == "mxfp4" else store(kI, sp.index_format, 0)
     win = O.compress(H, inp["W_win"], None, None, 1, d_r=sp.d_r, pos_stride=1, pos_offset=0)
     out["win"] = store(win, sp.kv_format, sp.d_r)
     return out
@@ -124,7 +124,12 @@ def prefill_reference(inp, caches, rows):
         d = dict(pos=p)
         if sp.nI:
             nv = int(O.n_visible(p, sp.m, T // sp.m))
-            s = O.index_scores(inp["qI"][r], inp["w"][r], caches["kI"], nv)
+            if sp.index_format == "mxfp4":
+                # quantised-oracle mode: the same E2M1 values and scales, fp64, bf16 scores
+                qq = mxfp4_values(inp["qI"][r])[0]
+                s = F.bf16_round(O.index_scores(qq, inp["w"][r], caches["kI"], nv))
+            else:
+                s = O.index_scores(inp["qI"][r], inp["w"][r], caches["kI"], nv)
             idx = O.topk(s, nv, sp.k)
             X = O.gather_rows(caches["kv"], idx, caches["win"], p, sp.n_win, T)
             d.update(scores=s, n_vis=nv, idx=idx)

@@ -11,7 +11,7 @@ import csa_inputs as I
 from long_context_sparse_10_amd import pipeline as G
 from oracle import csa as O
 from oracle import pipeline as OP
-from tests.gpu_util import dev, mx_score_bound, np64, report, score_error_bound
+from tests.gpu_util import bf16_ulp, dev, mx_score_bound, np64, report, score_error_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -133,3 +133,45 @@ def test_prefill_32k_full():
         report("prefill_32k", row=r, n_vis=nv, idx_exact=same, max_abs=err)
         assert err <= 2e-2
     report("prefill_32k", rows=len(rows), idx_exact=exact)
+
+
+def test_prefill_mxfp4_indexer_4k():
+    """The prefill with MXFP4 index keys and queries (4,096 tokens, compression
+    on the GPU).  Scores are checked in the quantised-oracle mode against the
+    GPU's own stored E2M1 codes and scales (fp64 products, bf16 scores); top-k
+    against those scores (bit-exact where tie-free); attention against the
+    oracle with the GPU's index sets."""
+    from oracle import formats as F
+    d = dev()
+    sp = I.CONFIGS["prefill_32k_mxfp4"]
+    T = 4096
+    inp = I.prefill_inputs(sp, T=T)
+    p = G.upload_prefill(inp, d)
+    G.prefill_compress(p)
+    G.prefill_attention_path(p)
+    torch.cuda.synchronize()
+    n = T // sp.m
+    kq = F.mxfp4_dequantize(p.kI.cpu().numpy().reshape(n, 64), p.kI_scale.cpu().numpy().reshape(n, 4))
+    qq = F.mxfp4_dequantize(p.qI.cpu().numpy().reshape(T, sp.nI, 64),
+                            p.qI_scale.cpu().numpy().reshape(T, sp.nI, 4))
+    caches = OP.prefill_caches(inp)
+    S = p.scores[0].double().cpu().numpy()
+    exact = 0
+    rows = [0, 3, 4, 7, 8, 127, 1000, 1023, 1024, 2049, 4095]
+    for r in rows:
+        pos = int(inp["q_pos"][r])
+        nv = int(O.n_visible(pos, sp.m, n))
+        ref = F.bf16_round(O.index_scores(qq[r], inp["w"][r], kq, nv))
+        e = score_error_bound(qq[r], inp["w"][r], kq, nv)
+        assert np.all(np.abs(S[r, :nv] - ref) <= bf16_ulp(np.abs(ref) + e) + e + 1e-30), r
+        got = p.idx[0, r].cpu().numpy()
+        bound = float((bf16_ulp(np.abs(ref) + e) + e).max()) if nv else 0.0
+        same = check_topk(got, ref, nv, sp.k, bound)
+        exact += same
+        X = O.gather_rows(caches["kv"], got, caches["win"], pos, sp.n_win, T)
+        want = O.attend_query(inp["q"][r], None, 1e-6, sp.d_r, 1e4, pos, X, inp["sink"],
+                              1 / np.sqrt(sp.c))
+        err = np.abs(p.out[0, r].double().cpu().numpy() - want).max()
+        report("prefill mxfp4 4k", row=r, n_vis=nv, idx_exact=same, max_abs=err)
+        assert err <= 2e-2
+    report("prefill mxfp4 4k", rows=len(rows), idx_exact=exact)

@@ -211,6 +211,47 @@ def test_indexer_bf16_query_rows(Tq, offset):
     report("indexer bf16 query rows", Tq=Tq, max_err=worst)
 
 
+@pytest.mark.parametrize("Tq,offset", [(1031, 0), (37, 4093)])
+def test_indexer_mxfp4_query_rows(Tq, offset):
+    """MXFP4 keys and queries with many query rows per sequence (the prefill
+    form of the block-scaled fp4 indexer): every visible bf16 score within one
+    bf16 step plus the fp32 accumulation bound of the quantised oracle (same
+    E2M1 values and scales in fp64, then bf16); beyond N(q) untouched."""
+    d = dev()
+    rng = np.random.default_rng(3 * Tq + offset)
+    B, nI, cI, m = 2, 64, 128, 4
+    N = (offset + Tq) // m + 3
+    kraw = rng.standard_normal((B, N, cI)).astype(np.float32)
+    qraw = rng.standard_normal((B, Tq, nI, cI)).astype(np.float32)
+    w = rng.standard_normal((B, Tq, nI)).astype(np.float32)
+    q_pos = (offset + np.arange(Tq, dtype=np.int32))[None].repeat(B, 0)
+    n_ent = np.array([N, N - 5], np.int32)
+    kI, kS = G.encode_rows(torch.from_numpy(kraw).to(d), L.MXFP4, B * N, cI)
+    qI, qS = G.encode_rows(torch.from_numpy(qraw).to(d), L.MXFP4, B * Tq * nI, cI)
+    scores = torch.full((B, Tq, N), float("nan"), dtype=torch.bfloat16, device=d)
+    L.indexer_score(qI, qS, L.MXFP4, torch.from_numpy(w).to(d), kI, kS, L.MXFP4,
+                    torch.from_numpy(q_pos).to(d), torch.from_numpy(n_ent).to(d), B, Tq, nI, cI,
+                    N, m, scores, L.BF16)
+    torch.cuda.synchronize()
+    S = np64(scores)
+    worst_ulps = 0.0
+    for b in range(B):
+        kq, _, _ = OP.mxfp4_values(kraw[b].astype(np.float64))
+        for t in list(range(0, Tq, 7)) + [Tq - 1]:
+            nv = int(O.n_visible(int(q_pos[b, t]), m, int(n_ent[b])))
+            qq, _, _ = OP.mxfp4_values(qraw[b, t].astype(np.float64))
+            ref = F.bf16_round(O.index_scores(qq, w[b, t].astype(np.float64), kq, nv))
+            err = np.abs(S[b, t, :nv] - ref)
+            # fp32 accumulation error of the exact E2M1 products, plus one bf16
+            # step (the two sides may round to neighbouring bf16 values)
+            e = score_error_bound(qq, w[b, t].astype(np.float64), kq, nv)
+            assert np.all(err <= bf16_ulp(np.abs(ref) + e) + e + 1e-30), (b, t)
+            assert np.all(np.isnan(S[b, t, nv:])), (b, t)
+            if nv:
+                worst_ulps = max(worst_ulps, float((err / bf16_ulp(ref)).max()))
+    report("indexer mxfp4 query rows", Tq=Tq, max_ulps=worst_ulps)
+
+
 def test_indexer_generic_f32_and_causal_prefill():
     d = dev()
     sp = I.CONFIGS["tiny_csa"]
