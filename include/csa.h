@@ -142,6 +142,35 @@ csa_status csa_compress(const void* H, csa_dtype h_t, int B, int T, int d,
                         void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /*
+ * csa_compress_append -- decode-time compression: the one new entry of each
+ * sequence whose latest block has just completed (Evidence Ledger Eqs 9-12,
+ * 20-26; the entry is formed exactly as csa_compress forms entry i, from the
+ * same candidates and in the same order, so the appended row equals the full
+ * pass's row i bit for bit).
+ *
+ *  H        [B, Tt, d] h_t: per sequence the tail of hidden states, Tt = 2m with
+ *           overlap (block i-1, then block i) or m without (block i).  For i = 0
+ *           the preceding-block rows are present but unused.
+ *  W_*, bias_*, m, overlap, c, norm_w, eps, rope_*, pos_stride, pos_offset:
+ *           as csa_compress (W_z_a and bias_a required).
+ *  entry    [B] int32 (device): the index i of the entry each sequence completes;
+ *           a sequence with i outside [0, Nmax) is skipped.
+ *  cache    [B, Nmax, row] in out_t; row entry[b] of sequence b is written,
+ *           nothing else.  cache_scale [B, Nmax, c/32] for CSA_MXFP4.
+ *  ws       fp32 projections of the tails: query with ws == NULL.
+ * Errors as csa_compress; asynchronous on `stream`.
+ */
+csa_status csa_compress_append(const void* H, csa_dtype h_t, int B, int d,
+                               const void* W_kv_a, const void* W_z_a,
+                               const void* W_kv_b, const void* W_z_b,
+                               const float* bias_a, const float* bias_b, int m, int overlap,
+                               int c, const float* norm_w, float eps, int rope_dims,
+                               float rope_theta, int pos_stride, int pos_offset,
+                               const int32_t* entry, void* cache, uint8_t* cache_scale,
+                               csa_dtype out_t, int Nmax, void* ws, size_t* ws_bytes,
+                               hipStream_t stream);
+
+/*
  * indexer_score -- lightning-indexer scores (Evidence Ledger Eqs 13-17;
  * shuhuayu section 03 score formula):
  *

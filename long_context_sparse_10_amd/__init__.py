@@ -7,7 +7,8 @@ The five calls of the path -- ``csa_compress``, ``indexer_score``,
 of device pointers.  See ``include/csa.h`` for the contract of each call.
 """
 from ._lib import (  # noqa: F401
-    BF16, F32, FP8MIX, MXFP4, CsaError, LIB_PATH, csa_compress, csa_prep_rows, hca_attend,
+    BF16, F32, FP8MIX, MXFP4, CsaError, LIB_PATH, csa_compress, csa_compress_append,
+    csa_prep_rows, hca_attend,
     indexer_score, lib, sparse_mqa_attend, status_string, topk_select, version,
 )
 

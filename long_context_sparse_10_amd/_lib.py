@@ -28,6 +28,9 @@ SIGNATURES = {
                       _vp, _vp, _i32, _vp],
     "csa_compress": [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                      _vp, _f32, _i32, _f32, _i32, _i32, _vp, _vp, _i32, _vp, _psz, _vp],
+    "csa_compress_append": [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                            _vp, _f32, _i32, _f32, _i32, _i32, _vp, _vp, _vp, _i32, _i32, _vp,
+                            _psz, _vp],
     "indexer_score": [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                       _i32, _i32, _vp, _i32, _vp],
     "topk_select": [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _psz, _vp],
@@ -134,6 +137,22 @@ def csa_compress(H, h_t, B, T, d, W_kv_a, W_z_a, W_kv_b, W_z_b, bias_a, bias_b, 
                               wp, szp, sid)
     st, ws = _workspace(call, H.device, ws)
     _check("csa_compress", st)
+    return ws
+
+
+def csa_compress_append(H, h_t, B, d, W_kv_a, W_z_a, W_kv_b, W_z_b, bias_a, bias_b, m, overlap, c,
+                        norm_w, eps, rope_dims, rope_theta, pos_stride, pos_offset, entry, cache,
+                        cache_scale, out_t, Nmax, ws=None, stream=None):
+    L = lib()
+    sid = _s(stream)
+
+    def call(wp, szp):
+        return L.csa_compress_append(_p(H), h_t, B, d, _p(W_kv_a), _p(W_z_a), _p(W_kv_b),
+                                     _p(W_z_b), _p(bias_a), _p(bias_b), m, overlap, c, _p(norm_w),
+                                     eps, rope_dims, rope_theta, pos_stride, pos_offset, _p(entry),
+                                     _p(cache), _p(cache_scale), out_t, Nmax, wp, szp, sid)
+    st, ws = _workspace(call, H.device, ws)
+    _check("csa_compress_append", st)
     return ws
 
 

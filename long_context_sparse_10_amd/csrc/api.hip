@@ -140,6 +140,40 @@ csa_status csa_compress(const void* H, csa_dtype h_t, int B, int T, int d, const
                                    out, out_scale, out_t, stream));
 }
 
+csa_status csa_compress_append(const void* H, csa_dtype h_t, int B, int d, const void* W_kv_a,
+                               const void* W_z_a, const void* W_kv_b, const void* W_z_b,
+                               const float* bias_a, const float* bias_b, int m, int overlap, int c,
+                               const float* norm_w, float eps, int rope_dims, float rope_theta,
+                               int pos_stride, int pos_offset, const int32_t* entry,
+                               void* cache, uint8_t* cache_scale, csa_dtype out_t, int Nmax,
+                               void* ws, size_t* ws_bytes, hipStream_t stream) {
+  if (!is_f32_bf16(h_t)) return CSA_ERR_UNSUPPORTED;
+  csa_status st = check_row_out(out_t, c, rope_dims, rope_theta, eps, cache, cache_scale);
+  if (st != CSA_OK) return st;
+  if (H == nullptr || W_kv_a == nullptr || W_z_a == nullptr || bias_a == nullptr ||
+      entry == nullptr)
+    return CSA_ERR_INVALID;
+  if (B < 0 || d <= 0 || m <= 0 || Nmax <= 0) return CSA_ERR_INVALID;
+  if (overlap && (W_kv_b == nullptr || W_z_b == nullptr || bias_b == nullptr)) return CSA_ERR_INVALID;
+  if (!overlap && (W_kv_b != nullptr || W_z_b != nullptr)) return CSA_ERR_INVALID;
+  const int T = overlap ? 2 * m : m;  // tail rows per sequence
+  if ((int64_t)B * T > INT_MAX || (int64_t)B * Nmax > INT_MAX) return CSA_ERR_INVALID;
+  const int nproj = overlap ? 4 : 2;
+  const size_t slot = (size_t)B * T * c;
+  if (ws_query(ws, ws_bytes, slot * nproj * sizeof(float), &st)) return st;
+  if (B == 0) return CSA_OK;
+  float* P = (float*)ws;
+  const void* Ws[4] = {W_kv_a, W_z_a, W_kv_b, W_z_b};
+  for (int i = 0; i < nproj; ++i) {
+    const hipError_t e = launch_gemm(H, Ws[i], h_t, P + i * slot, B * T, c, d, stream);
+    if (e != hipSuccess) return CSA_ERR_LAUNCH;
+  }
+  return launch_status(launch_pool(P, P + slot, overlap ? P + 2 * slot : nullptr,
+                                   overlap ? P + 3 * slot : nullptr, bias_a, bias_b, B, T, m, c,
+                                   norm_w, eps, rope_dims, rope_theta, pos_stride, pos_offset,
+                                   cache, cache_scale, out_t, stream, entry, Nmax));
+}
+
 csa_status indexer_score(const void* qI, const uint8_t* qI_scale, csa_dtype qI_t, const float* w,
                          const void* kI, const uint8_t* kI_scale, csa_dtype kI_t,
                          const int32_t* q_pos, const int32_t* n_entries, int B, int Tq, int nI,

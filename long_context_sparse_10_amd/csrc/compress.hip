@@ -214,17 +214,26 @@ hipError_t launch_gemm(const void* A, const void* Bm, csa_dtype t, float* C, int
 //   preceding block Z^b[m(i-1) + u, j] + bias_b[u, j] -> C^b[m(i-1) + u, j]  (overlap, i > 0)
 // by a max-subtracted softmax over the candidates; Za == NULL means m == 1
 // with a single candidate (the entry is C^a's row).
+// Append mode (entry != NULL): each sequence's T rows are only the tail -- the
+// preceding block (overlap) then the block just completed -- and its one new
+// entry is entry[b], written to row entry[b] of that sequence's Nmax cache
+// rows.  The candidates and the order of every operation are those of the
+// full pass, so the appended row equals the full pass's row bit for bit.
 __global__ __launch_bounds__(256) void pool_kernel(
     const float* __restrict__ Ca, const float* __restrict__ Za, const float* __restrict__ Cb,
     const float* __restrict__ Zb, const float* __restrict__ bias_a,
     const float* __restrict__ bias_b, int T, int m, int c, const float* __restrict__ norm_w,
     float eps, int d_r, Rope rt, int pos_stride, int pos_offset, uint8_t* __restrict__ out,
-    uint8_t* __restrict__ out_scale, csa_dtype out_t) {
+    uint8_t* __restrict__ out_scale, csa_dtype out_t, const int32_t* __restrict__ entry,
+    int Nmax) {
   extern __shared__ float smem[];
   float* row = smem;
   float* red = smem + c;
-  const int i = blockIdx.x, b = blockIdx.y;
-  const int n_out = T / m;
+  const int b = blockIdx.y;
+  const int i = entry != nullptr ? entry[b] : blockIdx.x;  // entry index in the sequence
+  if (entry != nullptr && (i < 0 || i >= Nmax)) return;
+  const int own0 = entry != nullptr ? T - m : m * i;        // first row of the own block
+  const int prv0 = entry != nullptr ? 0 : m * (i - 1);      // first row of the preceding block
   const int64_t base = (int64_t)b * T * c;
   const bool prev = (Cb != nullptr) && i > 0;
   for (int j = threadIdx.x; j < c; j += blockDim.x) {
@@ -234,20 +243,20 @@ __global__ __launch_bounds__(256) void pool_kernel(
     }
     float mx = -INFINITY;
     for (int u = 0; u < m; ++u)
-      mx = fmaxf(mx, Za[base + (int64_t)(m * i + u) * c + j] + bias_a[u * c + j]);
+      mx = fmaxf(mx, Za[base + (int64_t)(own0 + u) * c + j] + bias_a[u * c + j]);
     if (prev)
       for (int u = 0; u < m; ++u)
-        mx = fmaxf(mx, Zb[base + (int64_t)(m * (i - 1) + u) * c + j] + bias_b[u * c + j]);
+        mx = fmaxf(mx, Zb[base + (int64_t)(prv0 + u) * c + j] + bias_b[u * c + j]);
     float den = 0.f, num = 0.f;
     for (int u = 0; u < m; ++u) {
-      const int64_t t = base + (int64_t)(m * i + u) * c + j;
+      const int64_t t = base + (int64_t)(own0 + u) * c + j;
       const float e = expf(Za[t] + bias_a[u * c + j] - mx);
       den += e;
       num = fmaf(e, Ca[t], num);
     }
     if (prev)
       for (int u = 0; u < m; ++u) {
-        const int64_t t = base + (int64_t)(m * (i - 1) + u) * c + j;
+        const int64_t t = base + (int64_t)(prv0 + u) * c + j;
         const float e = expf(Zb[t] + bias_b[u * c + j] - mx);
         den += e;
         num = fmaf(e, Cb[t], num);
@@ -255,7 +264,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
     row[j] = num / den;
   }
   __syncthreads();
-  const int64_t r = (int64_t)b * n_out + i;
+  const int64_t r = (int64_t)b * (entry != nullptr ? Nmax : T / m) + i;
   const int64_t ob = row_bytes(out_t, c, d_r);
   finish_row(row, c, norm_w, eps, d_r, rt, (double)pos_stride * i + pos_offset, out + r * ob,
              out_t == CSA_MXFP4 ? out_scale + r * (c / 32) : nullptr, out_t, red);
@@ -265,14 +274,14 @@ hipError_t launch_pool(const float* Ca, const float* Za, const float* Cb, const 
                        const float* bias_a, const float* bias_b, int B, int T, int m, int c,
                        const float* norm_w, float eps, int rope_dims, float rope_theta,
                        int pos_stride, int pos_offset, void* out, uint8_t* out_scale,
-                       csa_dtype out_t, hipStream_t s) {
-  const int n_out = T / m;
+                       csa_dtype out_t, hipStream_t s, const int32_t* entry, int Nmax) {
+  const int n_out = entry != nullptr ? 1 : T / m;
   if (n_out == 0 || B == 0) return hipSuccess;
   const size_t shm = (size_t)(c + 16) * sizeof(float);
   hipLaunchKernelGGL(pool_kernel, dim3(n_out, B), dim3(256), shm, s, Ca, Za, Cb, Zb, bias_a,
                      bias_b, T, m, c, norm_w, eps, rope_dims,
                      make_rope(rope_dims, rope_theta), pos_stride, pos_offset,
-                     (uint8_t*)out, out_scale, out_t);
+                     (uint8_t*)out, out_scale, out_t, entry, Nmax);
   return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ hipError_t launch_pool(const float* Ca, const float* Za, const float* Cb, const 
                        const float* bias_a, const float* bias_b, int B, int T, int m, int c,
                        const float* norm_w, float eps, int rope_dims, float rope_theta,
                        int pos_stride, int pos_offset, void* out, uint8_t* out_scale,
-                       csa_dtype out_t, hipStream_t s);
+                       csa_dtype out_t, hipStream_t s, const int32_t* entry = nullptr,
+                       int Nmax = 0);
 
 // indexer.hip ---------------------------------------------------------------
 hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_t, const float* w,

@@ -27,7 +27,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = L.lib()
     names = declared_functions()
     assert set(names) == {"csa_version", "csa_status_string", "csa_prep_rows", "csa_compress",
-                          "indexer_score", "topk_select", "sparse_mqa_attend", "hca_attend"}
+                          "csa_compress_append", "indexer_score", "topk_select",
+                          "sparse_mqa_attend", "hca_attend"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -173,3 +174,23 @@ def test_attend_workspace_depends_on_slots_not_batch():
     assert need.value == 0                                    # many query rows: no split
     small = ctypes.c_size_t(1)
     assert _attend(ws=D, ws_bytes=ctypes.byref(small)) == _lib.ERR_WORKSPACE
+
+
+def test_compress_append_validation_and_workspace():
+    f = L.lib().csa_compress_append
+
+    def call(H=D, W_z_a=D, Wb=D, bias_b=D, overlap=1, B=4, m=4, entry=D, cache=D, Nmax=100,
+             ws=None, szp=None, out_t=L.BF16):
+        return f(H, L.BF16, B, 256, D, W_z_a, Wb, Wb, D, bias_b, m, overlap, 64, None, 1e-6, 16,
+                 1e4, m, 0, entry, cache, None, out_t, Nmax, ws, szp, None)
+    need = ctypes.c_size_t(0)
+    assert call(szp=ctypes.byref(need)) == _lib.OK
+    assert need.value == 4 * 4 * (2 * 4) * 64 * 4          # 4 projections of B * 2m rows, fp32
+    assert call(overlap=0, Wb=None, bias_b=None, szp=ctypes.byref(need)) == _lib.OK
+    assert need.value == 2 * 4 * 4 * 64 * 4                # 2 projections of B * m rows
+    assert call(entry=None) == _lib.ERR_INVALID
+    assert call(W_z_a=None) == _lib.ERR_INVALID
+    assert call(Nmax=0) == _lib.ERR_INVALID
+    assert call(overlap=0) == _lib.ERR_INVALID              # b-series weights without overlap
+    assert call(out_t=L.MXFP4) == _lib.ERR_INVALID          # MXFP4 needs a scale array
+    assert call() == _lib.ERR_WORKSPACE                     # workspace needed, none given

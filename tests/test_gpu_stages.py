@@ -414,3 +414,91 @@ def test_attend_fp8_rows_decode_every_code(k, slot):
     want = F.e4m3_decode(body)                                                    # [2, 448]
     report("attend fp8 codes", k=k, exact=bool(np.array_equal(got, np.broadcast_to(want[:, None], got.shape))))
     np.testing.assert_array_equal(got, np.broadcast_to(want[:, None, :], got.shape))
+
+
+# =================================================================== decode-time compression
+def _append_case(p, inp, sp, which, entries, out_t, Nmax):
+    """Run csa_compress_append for sequences completing ``entries`` (all
+    cut from the one prefill sequence) and return (cache, scales, full rows)."""
+    d_ = p.H.device
+    m = sp.m
+    overlap = m == 4
+    H = p.H.float() if p.H.dtype == torch.float32 else p.H
+    Tt = 2 * m if overlap else m
+    tails = []
+    for i in entries:
+        lo = m * i + m - Tt
+        t = torch.zeros(Tt, sp.d, dtype=H.dtype, device=d_)
+        src = H[max(lo, 0): m * i + m]
+        t[Tt - src.shape[0]:] = src
+        tails.append(t)
+    Ht = torch.stack(tails)
+    W = p.W
+    if which == "main":
+        Ws = (W["W_kv_a"], W["W_z_a"], W.get("W_kv_b"), W.get("W_z_b"), W["bias_a"], W.get("bias_b"))
+        c, d_r, norm = sp.c, sp.d_r, p.gamma
+    else:
+        Ws = (W["WI_kv_a"], W["WI_z_a"], W["WI_kv_b"], W["WI_z_b"], W["biasI_a"], W["biasI_b"])
+        c, d_r, norm = sp.cI, 0, None
+    B = len(entries)
+    rb = L.row_bytes(out_t, c, d_r)
+    cache = torch.full((B * Nmax * rb,), 0xAB, dtype=torch.uint8, device=d_)
+    scales = torch.full((B * Nmax * (c // 32),), 0xCD, dtype=torch.uint8, device=d_) if out_t == L.MXFP4 else None
+    entry = torch.tensor(entries, dtype=torch.int32, device=d_)
+    ht = L.F32 if Ht.dtype == torch.float32 else L.BF16
+    L.csa_compress_append(Ht, ht, B, sp.d, Ws[0], Ws[1], Ws[2] if overlap else None,
+                          Ws[3] if overlap else None, Ws[4], Ws[5] if overlap else None, m,
+                          int(overlap), c, norm, 1e-6, d_r, 1e4, m, 0, entry, cache, scales, out_t,
+                          Nmax)
+    torch.cuda.synchronize()
+    return cache.view(B, Nmax, rb), None if scales is None else scales.view(B, Nmax, c // 32), rb
+
+
+@pytest.mark.parametrize("name", ["tiny_csa", "tiny_hca"])
+def test_compress_append_tiny_f32(name):
+    """Appending entry i from the tail of hidden states reproduces the full
+    compressor's row i bit for bit and the oracle's entry within 1e-5; no
+    other cache row is touched."""
+    d = dev()
+    sp = I.CONFIGS[name]
+    inp = I.prefill_inputs(sp)
+    p = G.upload_prefill(inp, d)
+    G.prefill_compress(p)
+    torch.cuda.synchronize()
+    n = sp.T // sp.m
+    ref = OP.prefill_caches(inp)
+    entries = [0, 1, min(137, n - 1), n - 1]
+    cache, _, rb = _append_case(p, inp, sp, "main", entries, L.F32, n)
+    full = p.kv.view(n, rb)
+    worst = 0.0
+    for b, i in enumerate(entries):
+        assert torch.equal(cache[b, i], full[i]), (b, i)
+        got = cache[b, i].view(torch.float32).double().cpu().numpy()
+        worst = max(worst, float(np.abs(got - ref["kv"][i]).max()))
+        others = torch.cat([cache[b, :i], cache[b, i + 1:]])
+        assert bool((others == 0xAB).all()), (b, i)
+    report("compress append", cfg=name, max_abs_vs_oracle=worst)
+    assert worst <= 1e-5
+
+
+def test_compress_append_bf16_and_mxfp4_index_keys():
+    """bf16 hidden states and weights (the prefill shape, 4,096 tokens):
+    main entries in bf16 and MXFP4 index keys appended from tails equal the full
+    compressor's rows and scales bit for bit."""
+    d = dev()
+    sp = I.CONFIGS["prefill_32k_mxfp4"]
+    inp = I.prefill_inputs(sp, T=4096)
+    p = G.upload_prefill(inp, d)
+    G.prefill_compress(p)
+    torch.cuda.synchronize()
+    n = 4096 // sp.m
+    entries = [0, 1, 500, n - 1]
+    cache, _, rb = _append_case(p, inp, sp, "main", entries, L.BF16, n)
+    full = p.kv.view(n, rb)
+    for b, i in enumerate(entries):
+        assert torch.equal(cache[b, i], full[i]), ("main", b, i)
+    cI, sI, rbI = _append_case(p, inp, sp, "index", entries, L.MXFP4, n)
+    fullI, fullS = p.kI.view(n, rbI), p.kI_scale.view(n, sp.cI // 32)
+    for b, i in enumerate(entries):
+        assert torch.equal(cI[b, i], fullI[i]) and torch.equal(sI[b, i], fullS[i]), ("index", b, i)
+    report("compress append bf16 / mxfp4", entries=entries, bit_exact=True)
