@@ -269,18 +269,23 @@ __device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
 //    The rows feeding S^T are permuted (lane li reads entry 8(li/4) + 4nt + li%4)
 //    so that each lane's S^T results are exactly the P^T operand it needs
 //    (entries 8g..8g+7 of head li): nothing moves between the two contractions.
-//  * waves 4-7 (loaders): wave 4+w gathers rows 8w..8w+7 of every tile two
-//    tiles ahead into registers (expanding e4m3 to bf16) and commits them to
-//    the LDS tile the math waves are not using.
+//  * waves 4-7 (loaders): wave 4+w gathers rows 8w..8w+7 of every tile into
+//    registers, up to two tiles ahead of the one being committed, and commits
+//    them (expanding e4m3 to bf16) to the LDS tile the math waves are not using.
 // One barrier per tile separates the two buffers.
 template <int KVF>
 __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt, int chunk,
                                                          int nsplit, void* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) AttendSmem sm;
   const int hgroups = a.nh / 64;
-  const int split = blockIdx.x % nsplit;
-  const int hg = (blockIdx.x / nsplit) % hgroups;
-  const int row = blockIdx.x / (nsplit * hgroups);
+  // Workgroups are dealt to the 8 XCDs round-robin (block i runs on XCD i % 8).
+  // All splits and head groups of query row r go to XCD r % 8, so the row's
+  // queries and selected KV rows are fetched into one L2 and shared there.
+  const int xcd = blockIdx.x & 7, xj = blockIdx.x >> 3;
+  const int split = xj % nsplit;
+  const int hg = (xj / nsplit) % hgroups;
+  const int row = (xj / (nsplit * hgroups)) * 8 + xcd;
+  if (row >= a.B * a.Tq) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool math = wave < 4;
   const int mw = wave & 3;  // math: head group of the wave; loader: its rows 8mw..8mw+7
@@ -524,33 +529,30 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   }
 
   if (!math) {
-    // ---- loaders: a ring of 4 register sets keeps 4 tiles in flight; tile u
-    // lives in set u % 4.  While the math waves compute tile t from X[t & 1],
-    // tile t+1 is committed into X[(t+1) & 1] and tile t+5 is fetched into
-    // the set it frees.  The barrier count matches the math waves': one, then
-    // one per tile.
-    u32x4 st0[8], st1[8], st2[8], st3[8];
-    uint32_t ok0 = 0u, ok1 = 0u, ok2 = 0u, ok3 = 0u;
+    // ---- loaders: a ring of 2 register sets; tile u lives in set u % 2.
+    // While the math waves compute tile t from X[t & 1], tile t+1 is committed
+    // into X[(t+1) & 1] and tile t+3 is fetched into the set it frees.  Two
+    // tiles in flight per block already keep HBM busy with every CU loading,
+    // and a shallower ring brings each block's first tile back sooner.  The
+    // barrier count matches the math waves': one, then one per tile.
+    u32x4 st0[8], st1[8];
+    uint32_t ok0 = 0u, ok1 = 0u;
     CSA_STAGE(st0, ok0, 0);
     CSA_STAGE(st1, ok1, 1);
-    CSA_STAGE(st2, ok2, 2);
-    CSA_STAGE(st3, ok3, 3);
     CSA_QPREP();
     if (ntiles > 0) CSA_COMMIT(st0, ok0, 0);
-    CSA_STAGE(st0, ok0, 4);
+    CSA_STAGE(st0, ok0, 2);
     __syncthreads();
 #define CSA_PHASE(STG, OK, J)                                                                \
     if (t + (J) < ntiles) {                                                                  \
-      CSA_COMMIT(STG, OK, (J) & 1);                                                          \
-      CSA_STAGE(STG, OK, t + (J) + 4);                                                       \
+      CSA_COMMIT(STG, OK, (t + (J)) & 1);                                                    \
+      CSA_STAGE(STG, OK, t + (J) + 2);                                                       \
     }                                                                                        \
     __syncthreads();                                                                         \
     if (t + (J) >= ntiles) break;
-    for (int t = 0; t < ntiles; t += 4) {
+    for (int t = 0; t < ntiles; t += 2) {
       CSA_PHASE(st1, ok1, 1);
-      CSA_PHASE(st2, ok2, 2);
-      CSA_PHASE(st3, ok3, 3);
-      CSA_PHASE(st0, ok0, 4);
+      CSA_PHASE(st0, ok0, 2);
     }
 #undef CSA_PHASE
     return;
@@ -637,10 +639,12 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, Rope 
                                                              int nsplit,
                                                              const void* __restrict__ ws) {
   const int nh = a.nh, c = a.c, d_r = a.rope_dims;
-  const int row = blockIdx.x / nh, h = blockIdx.x % nh;
+  // the XCD that wrote row r's partials (r % 8) merges them
+  const int xj = blockIdx.x >> 3;
+  const int row = (xj / nh) * 8 + (blockIdx.x & 7), h = xj % nh;
   const int d = 2 * threadIdx.x;
-  if (d >= c) return;
   const int64_t nrows = (int64_t)a.B * a.Tq;
+  if (d >= c || row >= nrows) return;
   const uint16_t* wo = reinterpret_cast<const uint16_t*>(ws) + (int64_t)row * nsplit * nh * c;
   const float* wml = reinterpret_cast<const float*>(reinterpret_cast<const uint16_t*>(ws) +
                                                     nrows * nsplit * nh * c) +
@@ -732,14 +736,16 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s) {
   }
   int chunk, nsplit;
   plan_splits(a, &chunk, &nsplit);
-  dim3 grid((unsigned)((int64_t)nsplit * (a.nh / 64) * rows));
+  // rows rounded up to a multiple of 8 for the XCD-aware block order
+  const int64_t rows8 = (rows + 7) / 8 * 8;
+  dim3 grid((unsigned)((int64_t)nsplit * (a.nh / 64) * rows8));
   void* w = ws;
   if (a.kv_t == CSA_BF16)
     hipLaunchKernelGGL(attend_mfma_kernel<CSA_BF16>, grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   else
     hipLaunchKernelGGL(attend_mfma_kernel<CSA_FP8MIX>, grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   if (nsplit > 1)
-    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)((int64_t)rows * a.nh)),
+    hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)(rows8 * a.nh)),
                        dim3((a.c / 2 + 63) / 64 * 64), 0, s, a, rt, nsplit, (const void*)w);
   return hipGetLastError();
 }
