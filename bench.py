@@ -140,6 +140,8 @@ def run_decode(args, torch, I, G):
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         base = G.upload_decode(inp, dev, stream)
+        if args.paged:                           # caches moved into a hybrid page pool
+            G.page_decode(base, seed=1, drop_dense=True)
         copies = [base]
         for _ in range(args.copies - 1):
             c = G.Decode(**{k: getattr(base, k) for k in base.__dataclass_fields__})
@@ -148,6 +150,8 @@ def run_decode(args, torch, I, G):
                 v = getattr(base, name)
                 if v is not None:
                     setattr(c, name, v.clone())
+            if base.pool is not None:
+                c.pool = base.pool.clone()
             c.ws = None
             c.ws_topk = None
             copies.append(c)
@@ -227,7 +231,10 @@ def run_decode(args, torch, I, G):
         config=dict(workload=sp.name, batch=sp.B, context=sp.L, compressed_entries=N, m=sp.m,
                     heads=sp.nh, head_dim=sp.c, rope_dims=sp.d_r, top_k=sp.k or None,
                     indexer=(f"{sp.nI}x{sp.cI} {sp.index_format}" if sp.nI else None),
-                    kv_format=sp.kv_format, window=sp.n_win, cache_copies=args.copies),
+                    kv_format=sp.kv_format, window=sp.n_win, cache_copies=args.copies,
+                    cache=(f"paged: {base.pool.page_bytes}-byte pages of 32 CSA rows + 32 index "
+                           "keys + 1 HCA row, random page order" if base.pool is not None
+                           else "dense")),
         roofline=dict(bound="hbm", kernel=dom, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                       frac=achieved / HBM_PEAK_GBS, traffic=None,
                       algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=avg[dom]),
@@ -344,6 +351,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="decode: replay each step as a HIP graph")
     ap.add_argument("--chunks", type=int, default=1,
                     help="decode: batch groups whose chains run on two streams (1 = one chain)")
+    ap.add_argument("--paged", action="store_true",
+                    help="decode: caches in a hybrid page pool (block-table indirection)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration)")

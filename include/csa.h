@@ -262,6 +262,94 @@ csa_status hca_attend(const void* q, csa_dtype q_t, const float* q_norm_w, float
                       void* out, csa_dtype out_t,
                       void* ws, size_t* ws_bytes, hipStream_t stream);
 
+/*
+ * Paged caches (Evidence Ledger Section 3.5.1; shuhuayu section 06 "Hybrid
+ * attention creates a hybrid cache"): compressed entries live in fixed-size
+ * blocks covering lcm(m, m') tokens, so one block of 128 tokens holds 32 CSA
+ * entries (main rows and index keys) and 1 HCA entry.  A block is a PAGE of a
+ * caller-owned pool; the page holds each series in its own section at an
+ * offset the caller chooses.  A series is named by its base pointer -- the
+ * address of its slot 0 in page 0 (pool + section offset) -- and a csa_pages:
+ *
+ *   entry s of sequence b  ->  base + P * page_bytes + (s % E) * row_bytes,
+ *   P = block_table[b * max_blocks + s / E],  E = 2^entries_log2.
+ *
+ * MXFP4 scale rows (cI/32 bytes) are a series of their own with the same
+ * block table, page_bytes and E.  The sliding window stays in its dense ring
+ * (the fixed-size state cache).  Preconditions the library cannot check on the
+ * host: every block holding an entry the call reads or writes maps to a page
+ * of the pool, page 0 exists (empty attention slots read it and discard the
+ * data), and page ids are below 2^(31 - entries_log2).  Host checks: pages and
+ * block_table non-NULL, max_blocks >= 1, 0 <= entries_log2 <= 16,
+ * Nmax <= max_blocks * E, page_bytes a positive multiple of 16 with
+ * E * row_bytes <= page_bytes, series bases 16-byte aligned; else
+ * CSA_ERR_INVALID.  Results equal those of the dense calls on the same
+ * logical entries bit for bit.
+ */
+typedef struct csa_pages {
+  const int32_t* block_table; /* DEVICE [B, max_blocks] int32 page ids */
+  int max_blocks;             /* row stride of block_table */
+  int entries_log2;           /* log2 of the series' entries per page */
+  int64_t page_bytes;         /* bytes from one page to the next */
+} csa_pages;
+
+/* csa_compress into pages: `out` / `out_scale` are series bases; entry i of
+ * sequence b (i < T/m) is written to its page slot.  Nmax = T/m. */
+csa_status csa_compress_paged(const void* H, csa_dtype h_t, int B, int T, int d,
+                              const void* W_kv_a, const void* W_z_a,
+                              const void* W_kv_b, const void* W_z_b,
+                              const float* bias_a, const float* bias_b, int m, int overlap,
+                              int c, const float* norm_w, float eps, int rope_dims,
+                              float rope_theta, int pos_stride, int pos_offset,
+                              void* out, uint8_t* out_scale, csa_dtype out_t,
+                              const csa_pages* pages,
+                              void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* csa_compress_append into pages: `cache` / `cache_scale` are series bases. */
+csa_status csa_compress_append_paged(const void* H, csa_dtype h_t, int B, int d,
+                                     const void* W_kv_a, const void* W_z_a,
+                                     const void* W_kv_b, const void* W_z_b,
+                                     const float* bias_a, const float* bias_b, int m,
+                                     int overlap, int c, const float* norm_w, float eps,
+                                     int rope_dims, float rope_theta, int pos_stride,
+                                     int pos_offset, const int32_t* entry, void* cache,
+                                     uint8_t* cache_scale, csa_dtype out_t, int Nmax,
+                                     const csa_pages* pages,
+                                     void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* indexer_score over paged index keys: `kI` / `kI_scale` are series bases. */
+csa_status indexer_score_paged(const void* qI, const uint8_t* qI_scale, csa_dtype qI_t,
+                               const float* w,
+                               const void* kI, const uint8_t* kI_scale, csa_dtype kI_t,
+                               const csa_pages* pages,
+                               const int32_t* q_pos, const int32_t* n_entries,
+                               int B, int Tq, int nI, int cI, int Nmax, int m,
+                               void* scores, csa_dtype score_t, hipStream_t stream);
+
+/* sparse_mqa_attend over paged main rows: `kv` is a series base. */
+csa_status sparse_mqa_attend_paged(const void* q, csa_dtype q_t, const float* q_norm_w,
+                                   float eps, int rope_dims, float rope_theta,
+                                   const int32_t* q_pos,
+                                   const void* kv, csa_dtype kv_t, int Nmax,
+                                   const csa_pages* pages,
+                                   const int32_t* idx, int k,
+                                   const void* win, int win_len, int n_win,
+                                   const float* sink, float scale, int B, int Tq, int nh, int c,
+                                   void* out, csa_dtype out_t,
+                                   void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/* hca_attend over paged HCA rows (one entry per 128-token block:
+ * entries_log2 = 0 for m' = 128): `kv` is a series base. */
+csa_status hca_attend_paged(const void* q, csa_dtype q_t, const float* q_norm_w, float eps,
+                            int rope_dims, float rope_theta, const int32_t* q_pos,
+                            const void* kv, csa_dtype kv_t, int Nmax,
+                            const csa_pages* pages,
+                            const int32_t* n_entries, int m_prime,
+                            const void* win, int win_len, int n_win,
+                            const float* sink, float scale, int B, int Tq, int nh, int c,
+                            void* out, csa_dtype out_t,
+                            void* ws, size_t* ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

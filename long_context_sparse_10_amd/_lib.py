@@ -20,6 +20,15 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, 1, 2, 3, 4
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _psz = ctypes.POINTER(ctypes.c_size_t)
 
+
+class CsaPages(ctypes.Structure):
+    """struct csa_pages of include/csa.h."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int),
+                ("entries_log2", ctypes.c_int), ("page_bytes", ctypes.c_int64)]
+
+
+_pp = ctypes.POINTER(CsaPages)
+
 # name -> argument types, in the order of include/csa.h
 SIGNATURES = {
     "csa_version": [],
@@ -39,7 +48,35 @@ SIGNATURES = {
                           _psz, _vp],
     "hca_attend": [_vp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
                    _i32, _vp, _f32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _psz, _vp],
+    "csa_compress_paged": [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                           _i32, _vp, _f32, _i32, _f32, _i32, _i32, _vp, _vp, _i32, _pp, _vp,
+                           _psz, _vp],
+    "csa_compress_append_paged": [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                  _i32, _i32, _vp, _f32, _i32, _f32, _i32, _i32, _vp, _vp, _vp,
+                                  _i32, _i32, _pp, _vp, _psz, _vp],
+    "indexer_score_paged": [_vp, _vp, _i32, _vp, _vp, _vp, _i32, _pp, _vp, _vp, _i32, _i32, _i32,
+                            _i32, _i32, _i32, _vp, _i32, _vp],
+    "sparse_mqa_attend_paged": [_vp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _i32, _i32, _pp, _vp,
+                                _i32, _vp, _i32, _i32, _vp, _f32, _i32, _i32, _i32, _i32, _vp,
+                                _i32, _vp, _psz, _vp],
+    "hca_attend_paged": [_vp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _i32, _i32, _pp, _vp, _i32,
+                         _vp, _i32, _i32, _vp, _f32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _psz,
+                         _vp],
 }
+
+
+class Pages:
+    """A cache series held in pages: ``table`` is the device int32 block table
+    [B, max_blocks]; each page holds ``2**entries_log2`` entries of the series
+    and pages are ``page_bytes`` apart.  The series base (the address of slot 0
+    of page 0) is passed where the dense call takes the cache tensor."""
+
+    def __init__(self, table, entries_log2, page_bytes):
+        self.table, self.entries_log2, self.page_bytes = table, int(entries_log2), int(page_bytes)
+
+    def struct(self):
+        return CsaPages(_p(self.table), int(self.table.shape[-1]), self.entries_log2,
+                        self.page_bytes)
 
 _lib = None
 
@@ -126,42 +163,51 @@ def csa_prep_rows(x, x_t, rows, c, norm_w, eps, rope_dims, rope_theta, pos, rows
 
 def csa_compress(H, h_t, B, T, d, W_kv_a, W_z_a, W_kv_b, W_z_b, bias_a, bias_b, m, overlap, c,
                  norm_w, eps, rope_dims, rope_theta, pos_stride, pos_offset, out, out_scale, out_t,
-                 ws=None, stream=None):
+                 ws=None, stream=None, pages=None):
     L = lib()
     sid = _s(stream)
+    head = (_p(H), h_t, B, T, d, _p(W_kv_a), _p(W_z_a), _p(W_kv_b), _p(W_z_b), _p(bias_a),
+            _p(bias_b), m, overlap, c, _p(norm_w), eps, rope_dims, rope_theta, pos_stride,
+            pos_offset, _p(out), _p(out_scale), out_t)
+    ps = pages.struct() if pages is not None else None
 
     def call(wp, szp):
-        return L.csa_compress(_p(H), h_t, B, T, d, _p(W_kv_a), _p(W_z_a), _p(W_kv_b), _p(W_z_b),
-                              _p(bias_a), _p(bias_b), m, overlap, c, _p(norm_w), eps, rope_dims,
-                              rope_theta, pos_stride, pos_offset, _p(out), _p(out_scale), out_t,
-                              wp, szp, sid)
+        if ps is not None:
+            return L.csa_compress_paged(*head, ctypes.byref(ps), wp, szp, sid)
+        return L.csa_compress(*head, wp, szp, sid)
     st, ws = _workspace(call, H.device, ws)
-    _check("csa_compress", st)
+    _check("csa_compress_paged" if ps is not None else "csa_compress", st)
     return ws
 
 
 def csa_compress_append(H, h_t, B, d, W_kv_a, W_z_a, W_kv_b, W_z_b, bias_a, bias_b, m, overlap, c,
                         norm_w, eps, rope_dims, rope_theta, pos_stride, pos_offset, entry, cache,
-                        cache_scale, out_t, Nmax, ws=None, stream=None):
+                        cache_scale, out_t, Nmax, ws=None, stream=None, pages=None):
     L = lib()
     sid = _s(stream)
+    head = (_p(H), h_t, B, d, _p(W_kv_a), _p(W_z_a), _p(W_kv_b), _p(W_z_b), _p(bias_a),
+            _p(bias_b), m, overlap, c, _p(norm_w), eps, rope_dims, rope_theta, pos_stride,
+            pos_offset, _p(entry), _p(cache), _p(cache_scale), out_t, Nmax)
+    ps = pages.struct() if pages is not None else None
 
     def call(wp, szp):
-        return L.csa_compress_append(_p(H), h_t, B, d, _p(W_kv_a), _p(W_z_a), _p(W_kv_b),
-                                     _p(W_z_b), _p(bias_a), _p(bias_b), m, overlap, c, _p(norm_w),
-                                     eps, rope_dims, rope_theta, pos_stride, pos_offset, _p(entry),
-                                     _p(cache), _p(cache_scale), out_t, Nmax, wp, szp, sid)
+        if ps is not None:
+            return L.csa_compress_append_paged(*head, ctypes.byref(ps), wp, szp, sid)
+        return L.csa_compress_append(*head, wp, szp, sid)
     st, ws = _workspace(call, H.device, ws)
-    _check("csa_compress_append", st)
+    _check("csa_compress_append_paged" if ps is not None else "csa_compress_append", st)
     return ws
 
 
 def indexer_score(qI, qI_scale, qI_t, w, kI, kI_scale, kI_t, q_pos, n_entries, B, Tq, nI, cI,
-                  Nmax, m, scores, score_t, stream=None):
-    st = lib().indexer_score(_p(qI), _p(qI_scale), qI_t, _p(w), _p(kI), _p(kI_scale), kI_t,
-                             _p(q_pos), _p(n_entries), B, Tq, nI, cI, Nmax, m, _p(scores), score_t,
-                             _s(stream))
-    _check("indexer_score", st)
+                  Nmax, m, scores, score_t, stream=None, pages=None):
+    k = (_p(qI), _p(qI_scale), qI_t, _p(w), _p(kI), _p(kI_scale), kI_t)
+    tail = (_p(q_pos), _p(n_entries), B, Tq, nI, cI, Nmax, m, _p(scores), score_t, _s(stream))
+    if pages is not None:
+        ps = pages.struct()
+        _check("indexer_score_paged", lib().indexer_score_paged(*k, ctypes.byref(ps), *tail))
+    else:
+        _check("indexer_score", lib().indexer_score(*k, *tail))
 
 
 def topk_select(scores, score_t, q_pos, n_entries, B, Tq, Nmax, m, k, idx, ws=None, stream=None):
@@ -178,29 +224,36 @@ def topk_select(scores, score_t, q_pos, n_entries, B, Tq, Nmax, m, k, idx, ws=No
 
 def sparse_mqa_attend(q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, kv_t, Nmax, idx, k,
                       win, win_len, n_win, sink, scale, B, Tq, nh, c, out, out_t, ws=None,
-                      stream=None):
+                      stream=None, pages=None):
     L = lib()
     sid = _s(stream)
+    head = (_p(q), q_t, _p(q_norm_w), eps, rope_dims, rope_theta, _p(q_pos), _p(kv), kv_t, Nmax)
+    tail = (_p(idx), k, _p(win), win_len, n_win, _p(sink), scale, B, Tq, nh, c, _p(out), out_t)
+    ps = pages.struct() if pages is not None else None
 
     def call(wp, szp):
-        return L.sparse_mqa_attend(_p(q), q_t, _p(q_norm_w), eps, rope_dims, rope_theta, _p(q_pos),
-                                   _p(kv), kv_t, Nmax, _p(idx), k, _p(win), win_len, n_win,
-                                   _p(sink), scale, B, Tq, nh, c, _p(out), out_t, wp, szp, sid)
+        if ps is not None:
+            return L.sparse_mqa_attend_paged(*head, ctypes.byref(ps), *tail, wp, szp, sid)
+        return L.sparse_mqa_attend(*head, *tail, wp, szp, sid)
     st, ws = _workspace(call, q.device, ws)
-    _check("sparse_mqa_attend", st)
+    _check("sparse_mqa_attend_paged" if ps is not None else "sparse_mqa_attend", st)
     return ws
 
 
 def hca_attend(q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, kv_t, Nmax, n_entries,
                m_prime, win, win_len, n_win, sink, scale, B, Tq, nh, c, out, out_t, ws=None,
-               stream=None):
+               stream=None, pages=None):
     L = lib()
     sid = _s(stream)
+    head = (_p(q), q_t, _p(q_norm_w), eps, rope_dims, rope_theta, _p(q_pos), _p(kv), kv_t, Nmax)
+    tail = (_p(n_entries), m_prime, _p(win), win_len, n_win, _p(sink), scale, B, Tq, nh, c,
+            _p(out), out_t)
+    ps = pages.struct() if pages is not None else None
 
     def call(wp, szp):
-        return L.hca_attend(_p(q), q_t, _p(q_norm_w), eps, rope_dims, rope_theta, _p(q_pos), _p(kv),
-                            kv_t, Nmax, _p(n_entries), m_prime, _p(win), win_len, n_win, _p(sink),
-                            scale, B, Tq, nh, c, _p(out), out_t, wp, szp, sid)
+        if ps is not None:
+            return L.hca_attend_paged(*head, ctypes.byref(ps), *tail, wp, szp, sid)
+        return L.hca_attend(*head, *tail, wp, szp, sid)
     st, ws = _workspace(call, q.device, ws)
-    _check("hca_attend", st)
+    _check("hca_attend_paged" if ps is not None else "hca_attend", st)
     return ws

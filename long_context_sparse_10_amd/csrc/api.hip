@@ -52,6 +52,20 @@ bool ws_query(void* ws, size_t* ws_bytes, size_t need, csa_status* st) {
   return false;
 }
 
+// host checks of a paged series (rows of rb bytes, at most Nmax entries per
+// sequence, bases 16-byte aligned); *pg receives the kernels' view
+csa_status check_pages(const csa_pages* p, int Nmax, int64_t rb, const void* base,
+                       const void* base2, PageMap* pg) {
+  if (p == nullptr || p->block_table == nullptr || p->max_blocks < 1) return CSA_ERR_INVALID;
+  if (p->entries_log2 < 0 || p->entries_log2 > 16) return CSA_ERR_INVALID;
+  if (p->page_bytes <= 0 || p->page_bytes % 16 != 0) return CSA_ERR_INVALID;
+  if ((int64_t)Nmax > ((int64_t)p->max_blocks << p->entries_log2)) return CSA_ERR_INVALID;
+  if ((rb << p->entries_log2) > p->page_bytes) return CSA_ERR_INVALID;
+  if ((uintptr_t)base % 16 != 0 || (uintptr_t)base2 % 16 != 0) return CSA_ERR_INVALID;
+  *pg = PageMap{p->block_table, p->page_bytes, p->max_blocks, p->entries_log2};
+  return CSA_OK;
+}
+
 csa_status check_attend(const AttendArgs& a) {
   if (a.q == nullptr || a.q_pos == nullptr || a.kv == nullptr || a.sink == nullptr ||
       a.out == nullptr)
@@ -61,6 +75,9 @@ csa_status check_attend(const AttendArgs& a) {
   if (a.rope_dims < 0 || a.rope_dims > a.c || (a.rope_dims & 1)) return CSA_ERR_INVALID;
   if (a.rope_dims > 0 && !(a.rope_theta > 0.f)) return CSA_ERR_INVALID;
   if (!(a.eps >= 0.f)) return CSA_ERR_INVALID;
+  // slot tables hold int32 row ids
+  if (!a.pages.paged() && (int64_t)a.B * a.Nmax > INT_MAX) return CSA_ERR_INVALID;
+  if ((int64_t)a.B * a.win_len > INT_MAX - 2) return CSA_ERR_INVALID;
   if (a.n_win < 0 || (a.n_win > 0 && (a.win == nullptr || a.win_len < a.n_win))) return CSA_ERR_INVALID;
   if (!is_f32_bf16(a.q_t) || !is_f32_bf16(a.out_t)) return CSA_ERR_UNSUPPORTED;
   if (!(is_f32_bf16(a.kv_t) || a.kv_t == CSA_FP8MIX)) return CSA_ERR_UNSUPPORTED;
@@ -107,18 +124,28 @@ csa_status csa_prep_rows(const void* x, csa_dtype x_t, int64_t rows, int c, cons
                                         pos_offset, out, out_scale, out_t, stream));
 }
 
-csa_status csa_compress(const void* H, csa_dtype h_t, int B, int T, int d, const void* W_kv_a,
-                        const void* W_z_a, const void* W_kv_b, const void* W_z_b,
-                        const float* bias_a, const float* bias_b, int m, int overlap, int c,
-                        const float* norm_w, float eps, int rope_dims, float rope_theta,
-                        int pos_stride, int pos_offset, void* out, uint8_t* out_scale,
-                        csa_dtype out_t, void* ws, size_t* ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+static csa_status compress_impl(const void* H, csa_dtype h_t, int B, int T, int d,
+                                const void* W_kv_a, const void* W_z_a, const void* W_kv_b,
+                                const void* W_z_b, const float* bias_a, const float* bias_b,
+                                int m, int overlap, int c, const float* norm_w, float eps,
+                                int rope_dims, float rope_theta, int pos_stride, int pos_offset,
+                                void* out, uint8_t* out_scale, csa_dtype out_t,
+                                const csa_pages* pages, void* ws, size_t* ws_bytes,
+                                hipStream_t stream) {
   if (!is_f32_bf16(h_t)) return CSA_ERR_UNSUPPORTED;
   csa_status st = check_row_out(out_t, c, rope_dims, rope_theta, eps, out, out_scale);
   if (st != CSA_OK) return st;
   if (H == nullptr || W_kv_a == nullptr) return CSA_ERR_INVALID;
   if (B <= 0 || T <= 0 || d <= 0 || m <= 0) return CSA_ERR_INVALID;
   if ((int64_t)B * T > INT_MAX || (int64_t)B * (T / m) > (1ll << 24)) return CSA_ERR_INVALID;
+  PageMap pg = kDense;
+  if (pages != nullptr) {
+    st = check_pages(pages, T / m, row_bytes(out_t, c, rope_dims), out,
+                     out_t == CSA_MXFP4 ? out_scale : nullptr, &pg);
+    if (st != CSA_OK) return st;
+  }
   const bool single = (W_z_a == nullptr);
   if (single && (m != 1 || overlap)) return CSA_ERR_INVALID;
   if (!single && bias_a == nullptr) return CSA_ERR_INVALID;
@@ -137,16 +164,19 @@ csa_status csa_compress(const void* H, csa_dtype h_t, int B, int T, int d, const
   return launch_status(launch_pool(P, single ? nullptr : P + slot, overlap ? P + 2 * slot : nullptr,
                                    overlap ? P + 3 * slot : nullptr, bias_a, bias_b, B, T, m, c,
                                    norm_w, eps, rope_dims, rope_theta, pos_stride, pos_offset,
-                                   out, out_scale, out_t, stream));
+                                   out, out_scale, out_t, stream, nullptr, T / m, pg));
 }
 
-csa_status csa_compress_append(const void* H, csa_dtype h_t, int B, int d, const void* W_kv_a,
-                               const void* W_z_a, const void* W_kv_b, const void* W_z_b,
-                               const float* bias_a, const float* bias_b, int m, int overlap, int c,
-                               const float* norm_w, float eps, int rope_dims, float rope_theta,
-                               int pos_stride, int pos_offset, const int32_t* entry,
-                               void* cache, uint8_t* cache_scale, csa_dtype out_t, int Nmax,
-                               void* ws, size_t* ws_bytes, hipStream_t stream) {
+static csa_status compress_append_impl(const void* H, csa_dtype h_t, int B, int d,
+                                       const void* W_kv_a, const void* W_z_a,
+                                       const void* W_kv_b, const void* W_z_b,
+                                       const float* bias_a, const float* bias_b, int m,
+                                       int overlap, int c, const float* norm_w, float eps,
+                                       int rope_dims, float rope_theta, int pos_stride,
+                                       int pos_offset, const int32_t* entry, void* cache,
+                                       uint8_t* cache_scale, csa_dtype out_t, int Nmax,
+                                       const csa_pages* pages, void* ws, size_t* ws_bytes,
+                                       hipStream_t stream) {
   if (!is_f32_bf16(h_t)) return CSA_ERR_UNSUPPORTED;
   csa_status st = check_row_out(out_t, c, rope_dims, rope_theta, eps, cache, cache_scale);
   if (st != CSA_OK) return st;
@@ -158,6 +188,12 @@ csa_status csa_compress_append(const void* H, csa_dtype h_t, int B, int d, const
   if (!overlap && (W_kv_b != nullptr || W_z_b != nullptr)) return CSA_ERR_INVALID;
   const int T = overlap ? 2 * m : m;  // tail rows per sequence
   if ((int64_t)B * T > INT_MAX || (int64_t)B * Nmax > INT_MAX) return CSA_ERR_INVALID;
+  PageMap pg = kDense;
+  if (pages != nullptr) {
+    st = check_pages(pages, Nmax, row_bytes(out_t, c, rope_dims), cache,
+                     out_t == CSA_MXFP4 ? cache_scale : nullptr, &pg);
+    if (st != CSA_OK) return st;
+  }
   const int nproj = overlap ? 4 : 2;
   const size_t slot = (size_t)B * T * c;
   if (ws_query(ws, ws_bytes, slot * nproj * sizeof(float), &st)) return st;
@@ -171,14 +207,14 @@ csa_status csa_compress_append(const void* H, csa_dtype h_t, int B, int d, const
   return launch_status(launch_pool(P, P + slot, overlap ? P + 2 * slot : nullptr,
                                    overlap ? P + 3 * slot : nullptr, bias_a, bias_b, B, T, m, c,
                                    norm_w, eps, rope_dims, rope_theta, pos_stride, pos_offset,
-                                   cache, cache_scale, out_t, stream, entry, Nmax));
+                                   cache, cache_scale, out_t, stream, entry, Nmax, pg));
 }
 
-csa_status indexer_score(const void* qI, const uint8_t* qI_scale, csa_dtype qI_t, const float* w,
-                         const void* kI, const uint8_t* kI_scale, csa_dtype kI_t,
-                         const int32_t* q_pos, const int32_t* n_entries, int B, int Tq, int nI,
-                         int cI, int Nmax, int m, void* scores, csa_dtype score_t,
-                         hipStream_t stream) {
+static csa_status indexer_impl(const void* qI, const uint8_t* qI_scale, csa_dtype qI_t,
+                               const float* w, const void* kI, const uint8_t* kI_scale,
+                               csa_dtype kI_t, const csa_pages* pages, const int32_t* q_pos,
+                               const int32_t* n_entries, int B, int Tq, int nI, int cI, int Nmax,
+                               int m, void* scores, csa_dtype score_t, hipStream_t stream) {
   if (qI == nullptr || w == nullptr || kI == nullptr || q_pos == nullptr ||
       n_entries == nullptr || scores == nullptr)
     return CSA_ERR_INVALID;
@@ -190,9 +226,89 @@ csa_status indexer_score(const void* qI, const uint8_t* qI_scale, csa_dtype qI_t
   if (qI_t == CSA_MXFP4 && (cI % 32 != 0 || qI_scale == nullptr || kI_scale == nullptr))
     return CSA_ERR_INVALID;
   if ((int64_t)nI * cI > 15 * 1024) return CSA_ERR_UNSUPPORTED;
+  PageMap pg = kDense;
+  if (pages != nullptr) {
+    const csa_status st = check_pages(pages, Nmax, row_bytes(kI_t, cI, 0), kI,
+                                      qI_t == CSA_MXFP4 ? kI_scale : nullptr, &pg);
+    if (st != CSA_OK) return st;
+  }
   if (B == 0 || Tq == 0) return CSA_OK;
   return launch_status(launch_indexer(qI, qI_scale, qI_t, w, kI, kI_scale, q_pos, n_entries, B,
-                                      Tq, nI, cI, Nmax, m, scores, score_t, stream));
+                                      Tq, nI, cI, Nmax, m, scores, score_t, stream, pg));
+}
+
+extern "C" {
+
+csa_status csa_compress(const void* H, csa_dtype h_t, int B, int T, int d, const void* W_kv_a,
+                        const void* W_z_a, const void* W_kv_b, const void* W_z_b,
+                        const float* bias_a, const float* bias_b, int m, int overlap, int c,
+                        const float* norm_w, float eps, int rope_dims, float rope_theta,
+                        int pos_stride, int pos_offset, void* out, uint8_t* out_scale,
+                        csa_dtype out_t, void* ws, size_t* ws_bytes, hipStream_t stream) {
+  return compress_impl(H, h_t, B, T, d, W_kv_a, W_z_a, W_kv_b, W_z_b, bias_a, bias_b, m, overlap,
+                       c, norm_w, eps, rope_dims, rope_theta, pos_stride, pos_offset, out,
+                       out_scale, out_t, nullptr, ws, ws_bytes, stream);
+}
+
+csa_status csa_compress_paged(const void* H, csa_dtype h_t, int B, int T, int d,
+                              const void* W_kv_a, const void* W_z_a, const void* W_kv_b,
+                              const void* W_z_b, const float* bias_a, const float* bias_b, int m,
+                              int overlap, int c, const float* norm_w, float eps, int rope_dims,
+                              float rope_theta, int pos_stride, int pos_offset, void* out,
+                              uint8_t* out_scale, csa_dtype out_t, const csa_pages* pages,
+                              void* ws, size_t* ws_bytes, hipStream_t stream) {
+  if (pages == nullptr) return CSA_ERR_INVALID;
+  return compress_impl(H, h_t, B, T, d, W_kv_a, W_z_a, W_kv_b, W_z_b, bias_a, bias_b, m, overlap,
+                       c, norm_w, eps, rope_dims, rope_theta, pos_stride, pos_offset, out,
+                       out_scale, out_t, pages, ws, ws_bytes, stream);
+}
+
+csa_status csa_compress_append(const void* H, csa_dtype h_t, int B, int d, const void* W_kv_a,
+                               const void* W_z_a, const void* W_kv_b, const void* W_z_b,
+                               const float* bias_a, const float* bias_b, int m, int overlap, int c,
+                               const float* norm_w, float eps, int rope_dims, float rope_theta,
+                               int pos_stride, int pos_offset, const int32_t* entry,
+                               void* cache, uint8_t* cache_scale, csa_dtype out_t, int Nmax,
+                               void* ws, size_t* ws_bytes, hipStream_t stream) {
+  return compress_append_impl(H, h_t, B, d, W_kv_a, W_z_a, W_kv_b, W_z_b, bias_a, bias_b, m,
+                              overlap, c, norm_w, eps, rope_dims, rope_theta, pos_stride,
+                              pos_offset, entry, cache, cache_scale, out_t, Nmax, nullptr, ws,
+                              ws_bytes, stream);
+}
+
+csa_status csa_compress_append_paged(const void* H, csa_dtype h_t, int B, int d,
+                                     const void* W_kv_a, const void* W_z_a, const void* W_kv_b,
+                                     const void* W_z_b, const float* bias_a, const float* bias_b,
+                                     int m, int overlap, int c, const float* norm_w, float eps,
+                                     int rope_dims, float rope_theta, int pos_stride,
+                                     int pos_offset, const int32_t* entry, void* cache,
+                                     uint8_t* cache_scale, csa_dtype out_t, int Nmax,
+                                     const csa_pages* pages, void* ws, size_t* ws_bytes,
+                                     hipStream_t stream) {
+  if (pages == nullptr) return CSA_ERR_INVALID;
+  return compress_append_impl(H, h_t, B, d, W_kv_a, W_z_a, W_kv_b, W_z_b, bias_a, bias_b, m,
+                              overlap, c, norm_w, eps, rope_dims, rope_theta, pos_stride,
+                              pos_offset, entry, cache, cache_scale, out_t, Nmax, pages, ws,
+                              ws_bytes, stream);
+}
+
+csa_status indexer_score(const void* qI, const uint8_t* qI_scale, csa_dtype qI_t, const float* w,
+                         const void* kI, const uint8_t* kI_scale, csa_dtype kI_t,
+                         const int32_t* q_pos, const int32_t* n_entries, int B, int Tq, int nI,
+                         int cI, int Nmax, int m, void* scores, csa_dtype score_t,
+                         hipStream_t stream) {
+  return indexer_impl(qI, qI_scale, qI_t, w, kI, kI_scale, kI_t, nullptr, q_pos, n_entries, B, Tq,
+                      nI, cI, Nmax, m, scores, score_t, stream);
+}
+
+csa_status indexer_score_paged(const void* qI, const uint8_t* qI_scale, csa_dtype qI_t,
+                               const float* w, const void* kI, const uint8_t* kI_scale,
+                               csa_dtype kI_t, const csa_pages* pages, const int32_t* q_pos,
+                               const int32_t* n_entries, int B, int Tq, int nI, int cI, int Nmax,
+                               int m, void* scores, csa_dtype score_t, hipStream_t stream) {
+  if (pages == nullptr) return CSA_ERR_INVALID;
+  return indexer_impl(qI, qI_scale, qI_t, w, kI, kI_scale, kI_t, pages, q_pos, n_entries, B, Tq,
+                      nI, cI, Nmax, m, scores, score_t, stream);
 }
 
 csa_status topk_select(const void* scores, csa_dtype score_t, const int32_t* q_pos,
@@ -210,7 +326,14 @@ csa_status topk_select(const void* scores, csa_dtype score_t, const int32_t* q_p
                                    stream));
 }
 
-static csa_status attend_common(AttendArgs& a, void* ws, size_t* ws_bytes, hipStream_t stream) {
+static csa_status attend_common(AttendArgs& a, const csa_pages* pages, void* ws,
+                                size_t* ws_bytes, hipStream_t stream) {
+  a.pages = kDense;
+  if (pages != nullptr) {
+    const csa_status sp = check_pages(pages, a.Nmax, row_bytes(a.kv_t, a.c, a.rope_dims), a.kv,
+                                      nullptr, &a.pages);
+    if (sp != CSA_OK) return sp;
+  }
   csa_status st = check_attend(a);
   if (st != CSA_OK) return st;
   if (ws_query(ws, ws_bytes, attend_workspace(a), &st)) return st;
@@ -226,8 +349,22 @@ csa_status sparse_mqa_attend(const void* q, csa_dtype q_t, const float* q_norm_w
                              csa_dtype out_t, void* ws, size_t* ws_bytes, hipStream_t stream) {
   if (idx == nullptr) return CSA_ERR_INVALID;
   AttendArgs a{q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, kv_t, Nmax, idx, k,
-               nullptr, 0, win, win_len, n_win, sink, scale, B, Tq, nh, c, out, out_t};
-  return attend_common(a, ws, ws_bytes, stream);
+               nullptr, 0, win, win_len, n_win, sink, scale, B, Tq, nh, c, out, out_t, kDense};
+  return attend_common(a, nullptr, ws, ws_bytes, stream);
+}
+
+csa_status sparse_mqa_attend_paged(const void* q, csa_dtype q_t, const float* q_norm_w, float eps,
+                                   int rope_dims, float rope_theta, const int32_t* q_pos,
+                                   const void* kv, csa_dtype kv_t, int Nmax,
+                                   const csa_pages* pages, const int32_t* idx, int k,
+                                   const void* win, int win_len, int n_win, const float* sink,
+                                   float scale, int B, int Tq, int nh, int c, void* out,
+                                   csa_dtype out_t, void* ws, size_t* ws_bytes,
+                                   hipStream_t stream) {
+  if (idx == nullptr || pages == nullptr) return CSA_ERR_INVALID;
+  AttendArgs a{q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, kv_t, Nmax, idx, k,
+               nullptr, 0, win, win_len, n_win, sink, scale, B, Tq, nh, c, out, out_t, kDense};
+  return attend_common(a, pages, ws, ws_bytes, stream);
 }
 
 csa_status hca_attend(const void* q, csa_dtype q_t, const float* q_norm_w, float eps,
@@ -237,8 +374,23 @@ csa_status hca_attend(const void* q, csa_dtype q_t, const float* q_norm_w, float
                       int B, int Tq, int nh, int c, void* out, csa_dtype out_t, void* ws,
                       size_t* ws_bytes, hipStream_t stream) {
   AttendArgs a{q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, kv_t, Nmax, nullptr, 0,
-               n_entries, m_prime, win, win_len, n_win, sink, scale, B, Tq, nh, c, out, out_t};
-  return attend_common(a, ws, ws_bytes, stream);
+               n_entries, m_prime, win, win_len, n_win, sink, scale, B, Tq, nh, c, out, out_t,
+               kDense};
+  return attend_common(a, nullptr, ws, ws_bytes, stream);
+}
+
+csa_status hca_attend_paged(const void* q, csa_dtype q_t, const float* q_norm_w, float eps,
+                            int rope_dims, float rope_theta, const int32_t* q_pos, const void* kv,
+                            csa_dtype kv_t, int Nmax, const csa_pages* pages,
+                            const int32_t* n_entries, int m_prime, const void* win, int win_len,
+                            int n_win, const float* sink, float scale, int B, int Tq, int nh,
+                            int c, void* out, csa_dtype out_t, void* ws, size_t* ws_bytes,
+                            hipStream_t stream) {
+  if (pages == nullptr) return CSA_ERR_INVALID;
+  AttendArgs a{q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, kv_t, Nmax, nullptr, 0,
+               n_entries, m_prime, win, win_len, n_win, sink, scale, B, Tq, nh, c, out, out_t,
+               kDense};
+  return attend_common(a, pages, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -44,10 +44,10 @@ struct SlotCtx {
   const uint8_t* kv;
   const uint8_t* win;
   const int32_t* idx_row;  // sparse only
-  int64_t kv_base;         // b * Nmax
+  PageMap pg;              // kv rows: dense or paged
   int64_t win_base;        // b * win_len
   int64_t rb;              // bytes per row
-  int kslots, nv, qp, n_win, win_len, nmax;
+  int b, kslots, nv, qp, n_win, win_len, nmax;
   bool sparse;
   __device__ __forceinline__ const uint8_t* row(int v) const {
     if (v < kslots) {
@@ -58,7 +58,7 @@ struct SlotCtx {
       } else if (v >= nv) {
         return nullptr;
       }
-      return kv + (kv_base + s) * rb;
+      return kv + pg.off(b, s, nmax, rb);
     }
     const int pw = qp - n_win + 1 + (v - kslots);
     if (pw < 0 || v - kslots >= n_win) return nullptr;
@@ -73,7 +73,8 @@ __device__ __forceinline__ SlotCtx make_ctx(const AttendArgs& a, int row) {
   x.win = (const uint8_t*)a.win;
   x.sparse = a.idx != nullptr;
   x.idx_row = x.sparse ? a.idx + (int64_t)row * a.k : nullptr;
-  x.kv_base = (int64_t)b * a.Nmax;
+  x.pg = a.pages;
+  x.b = b;
   x.win_base = (int64_t)b * a.win_len;
   x.rb = row_bytes(a.kv_t, a.c, a.rope_dims);
   x.qp = a.q_pos[row];
@@ -189,11 +190,21 @@ __device__ __forceinline__ int slot_row_id(const SlotCtx& x, int v) {
     } else if (v >= x.nv) {
       return -1;
     }
-    return (int)(x.kv_base + s);
+    // dense: the row b * Nmax + s; paged: (page << shift) | slot, decoded by kv_addr
+    if (x.pg.paged()) return (x.pg.page(x.b, s) << x.pg.shift) | (s & ((1 << x.pg.shift) - 1));
+    return (int)((int64_t)x.b * x.nmax + s);
   }
   const int pw = x.qp - x.n_win + 1 + (v - x.kslots);
   if (pw < 0 || v - x.kslots >= x.n_win) return -1;
   return -2 - (int)(x.win_base + pw % x.win_len);
+}
+
+// address of the kv row a slot table id (>= 0) names
+__device__ __forceinline__ const uint8_t* kv_addr(const SlotCtx& x, int id) {
+  if (x.pg.paged())
+    return x.kv + (int64_t)(id >> x.pg.shift) * x.pg.page_bytes +
+           (int64_t)(id & ((1 << x.pg.shift) - 1)) * x.rb;
+  return x.kv + (int64_t)id * x.rb;
 }
 
 // Physical LDS row of tile entry e: a bit permutation (e4 -> bit 0, e0 -> 1,
@@ -405,7 +416,7 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
         OK |= (id != -1 ? 1u : 0u) << i;                                                     \
         const bool in_kv = id >= -1;                                                         \
         const int r = id >= 0 ? id : (id == -1 ? 0 : -2 - id);                               \
-        src[i] = (in_kv ? ctx.kv : ctx.win) + (int64_t)r * rb;                               \
+        src[i] = in_kv ? kv_addr(ctx, r) : ctx.win + (int64_t)r * rb;                        \
       }                                                                                      \
     }                                                                                        \
     /* bf16 rows: lane l takes bytes 16l..16l+15; FP8 rows (576 B): lanes    */            \

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
     const float* __restrict__ bias_b, int T, int m, int c, const float* __restrict__ norm_w,
     float eps, int d_r, Rope rt, int pos_stride, int pos_offset, uint8_t* __restrict__ out,
     uint8_t* __restrict__ out_scale, csa_dtype out_t, const int32_t* __restrict__ entry,
-    int Nmax) {
+    int Nmax, PageMap pg) {
   extern __shared__ float smem[];
   float* row = smem;
   float* red = smem + c;
@@ -264,24 +264,28 @@ __global__ __launch_bounds__(256) void pool_kernel(
     row[j] = num / den;
   }
   __syncthreads();
-  const int64_t r = (int64_t)b * (entry != nullptr ? Nmax : T / m) + i;
+  // the row (and the MXFP4 scales, a series of c/32-byte rows sharing the
+  // pages) of entry i of sequence b
+  const int nrows = entry != nullptr ? Nmax : T / m;
   const int64_t ob = row_bytes(out_t, c, d_r);
-  finish_row(row, c, norm_w, eps, d_r, rt, (double)pos_stride * i + pos_offset, out + r * ob,
-             out_t == CSA_MXFP4 ? out_scale + r * (c / 32) : nullptr, out_t, red);
+  finish_row(row, c, norm_w, eps, d_r, rt, (double)pos_stride * i + pos_offset,
+             out + pg.off(b, i, nrows, ob),
+             out_t == CSA_MXFP4 ? out_scale + pg.off(b, i, nrows, c / 32) : nullptr, out_t, red);
 }
 
 hipError_t launch_pool(const float* Ca, const float* Za, const float* Cb, const float* Zb,
                        const float* bias_a, const float* bias_b, int B, int T, int m, int c,
                        const float* norm_w, float eps, int rope_dims, float rope_theta,
                        int pos_stride, int pos_offset, void* out, uint8_t* out_scale,
-                       csa_dtype out_t, hipStream_t s, const int32_t* entry, int Nmax) {
+                       csa_dtype out_t, hipStream_t s, const int32_t* entry, int Nmax,
+                       const PageMap& pg) {
   const int n_out = entry != nullptr ? 1 : T / m;
   if (n_out == 0 || B == 0) return hipSuccess;
   const size_t shm = (size_t)(c + 16) * sizeof(float);
   hipLaunchKernelGGL(pool_kernel, dim3(n_out, B), dim3(256), shm, s, Ca, Za, Cb, Zb, bias_a,
                      bias_b, T, m, c, norm_w, eps, rope_dims,
                      make_rope(rope_dims, rope_theta), pos_stride, pos_offset,
-                     (uint8_t*)out, out_scale, out_t, entry, Nmax);
+                     (uint8_t*)out, out_scale, out_t, entry, Nmax, pg);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void indexer_generic_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale, csa_dtype t,
     const float* __restrict__ w, const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale,
     const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int Tq, int nI,
-    int cI, int Nmax, int m, void* __restrict__ scores, int score_bf16) {
+    int cI, int Nmax, int m, void* __restrict__ scores, int score_bf16, PageMap pg) {
   extern __shared__ float sq[];  // [nI * cI] query, then [nI] weights
   const int tiles = (Nmax + blockDim.x - 1) / blockDim.x;
   const int row = blockIdx.x / tiles, tile = blockIdx.x % tiles, b = row / Tq;
@@ -47,9 +47,8 @@ __global__ __launch_bounds__(256) void indexer_generic_kernel(
   __syncthreads();
   const int s = tile * blockDim.x + threadIdx.x;
   if (s >= nv) return;
-  const int64_t kr = (int64_t)b * Nmax + s;
-  const uint8_t* krow = kI + kr * qrb;
-  const uint8_t* ksc = kI_scale ? kI_scale + kr * (cI / 32) : nullptr;
+  const uint8_t* krow = kI + pg.off(b, s, Nmax, qrb);
+  const uint8_t* ksc = kI_scale ? kI_scale + pg.off(b, s, Nmax, cI / 32) : nullptr;
   float score = 0.f;
   for (int h = 0; h < nI; ++h) {
     float dot = 0.f;
@@ -91,8 +90,9 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
     const float* __restrict__ w, const uint8_t* __restrict__ kI,
     const uint8_t* __restrict__ kI_scale, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int Nmax, int m, int ent_per_block,
-    void* __restrict__ scores, int score_bf16) {
+    void* __restrict__ scores, int score_bf16, PageMap pg) {
   constexpr int G = MX ? 8 : 2;
+  constexpr int64_t RB = MX ? 64 : 256;  // key row bytes
   const int tiles = (Nmax + ent_per_block - 1) / ent_per_block;
   const int row = blockIdx.x / tiles, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -134,14 +134,33 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int n = base + 16 * g + col;
-      const int64_t kr = (int64_t)b * Nmax + (n < e1 ? n : e0);
+      // key row and scale row offsets: dense rows b * Nmax + n, or slot n % 2^shift of
+      // the page holding entry n (the scales share the key rows' pages)
+      int64_t ko, so;
+      if (pg.paged()) {
+        // a 16-entry group lies in one page (pages hold >= 16 entries, groups
+        // start at multiples of 16): one wave-uniform page id per group, a
+        // scalar load that does not wait behind the key loads in flight.
+        // Lanes past the visible range read the group's first row (or e0's).
+        const int gs = __builtin_amdgcn_readfirstlane(base) + 16 * g;
+        const int ge = gs < e1 ? gs : e0;
+        const int nn = n < e1 ? n : ge;
+        const int64_t pb = (int64_t)pg.page(b, ge) * pg.page_bytes;
+        const int sl = nn & ((1 << pg.shift) - 1);
+        ko = pb + (int64_t)sl * RB;
+        so = pb + (int64_t)sl * 4;
+      } else {
+        const int64_t kr = (int64_t)b * Nmax + (n < e1 ? n : e0);
+        ko = kr * RB;
+        so = kr * 4;
+      }
       if (!MX) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          r.v[4 * g + ks] = *reinterpret_cast<const u32x4*>(kI + kr * 256 + 64 * ks + 16 * kg);
+          r.v[4 * g + ks] = *reinterpret_cast<const u32x4*>(kI + ko + 64 * ks + 16 * kg);
       } else {
-        r.v[g] = *reinterpret_cast<const u32x4*>(kI + kr * 64 + 16 * kg);
-        r.sc[g] = *reinterpret_cast<const uint32_t*>(kI_scale + kr * 4);
+        r.v[g] = *reinterpret_cast<const u32x4*>(kI + ko + 16 * kg);
+        r.sc[g] = *reinterpret_cast<const uint32_t*>(kI_scale + so);
       }
     }
   };
@@ -413,22 +432,26 @@ __global__ __launch_bounds__(64 * R) void indexer_rows_mx_kernel(
 hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_t, const float* w,
                           const void* kI, const uint8_t* kI_scale, const int32_t* q_pos,
                           const int32_t* n_entries, int B, int Tq, int nI, int cI, int Nmax,
-                          int m, void* scores, csa_dtype score_t, hipStream_t s) {
+                          int m, void* scores, csa_dtype score_t, hipStream_t s,
+                          const PageMap& pg) {
   const int rows = B * Tq;
   if (rows == 0 || Nmax == 0) return hipSuccess;
   const int sbf = score_t == CSA_BF16;
-  if (in_t == CSA_BF16 && nI == 64 && cI == 128 && Tq >= IR_ROWS) {
+  // the many-query-row kernels stage dense key chunks; paged keys take the
+  // per-row kernel
+  if (in_t == CSA_BF16 && nI == 64 && cI == 128 && Tq >= IR_ROWS && !pg.paged()) {
     const int64_t groups = (int64_t)B * ((Tq + IR_ROWS - 1) / IR_ROWS);
     hipLaunchKernelGGL(indexer_rows_kernel<IR_ROWS>, dim3((unsigned)groups), dim3(64 * IR_ROWS), 0,
                        s, (const uint8_t*)qI, w, (const uint8_t*)kI, q_pos, n_entries, B, Tq,
                        Nmax, m, scores, sbf);
-  } else if (in_t == CSA_MXFP4 && nI == 64 && cI == 128 && Tq >= IR_ROWS) {
+  } else if (in_t == CSA_MXFP4 && nI == 64 && cI == 128 && Tq >= IR_ROWS && !pg.paged()) {
     const int64_t groups = (int64_t)B * ((Tq + IR_ROWS - 1) / IR_ROWS);
     hipLaunchKernelGGL(indexer_rows_mx_kernel<IR_ROWS>, dim3((unsigned)groups),
                        dim3(64 * IR_ROWS), 0, s, (const uint8_t*)qI, qI_scale, w,
                        (const uint8_t*)kI, kI_scale, q_pos, n_entries, B, Tq, Nmax, m, scores,
                        sbf);
-  } else if ((in_t == CSA_BF16 || in_t == CSA_MXFP4) && nI == 64 && cI == 128) {
+  } else if ((in_t == CSA_BF16 || in_t == CSA_MXFP4) && nI == 64 && cI == 128 &&
+             (!pg.paged() || pg.shift >= 4)) {
     // about two resident blocks per CU over the whole call; a block covers a
     // multiple of one step of its 4 waves (bf16 128 entries, MXFP4 512)
     const int step = in_t == CSA_MXFP4 ? 512 : 128;
@@ -439,17 +462,17 @@ hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_
     if (in_t == CSA_BF16)
       hipLaunchKernelGGL(indexer_mfma_kernel<false>, grid, dim3(IDX_WAVES * 64), 0, s,
                          (const uint8_t*)qI, qI_scale, w, (const uint8_t*)kI, kI_scale, q_pos,
-                         n_entries, Tq, Nmax, m, epb, scores, sbf);
+                         n_entries, Tq, Nmax, m, epb, scores, sbf, pg);
     else
       hipLaunchKernelGGL(indexer_mfma_kernel<true>, grid, dim3(IDX_WAVES * 64), 0, s,
                          (const uint8_t*)qI, qI_scale, w, (const uint8_t*)kI, kI_scale, q_pos,
-                         n_entries, Tq, Nmax, m, epb, scores, sbf);
+                         n_entries, Tq, Nmax, m, epb, scores, sbf, pg);
   } else {
     dim3 grid((unsigned)(((int64_t)Nmax + 255) / 256 * rows));
     const size_t shm = (size_t)(nI * cI + nI) * sizeof(float);
     hipLaunchKernelGGL(indexer_generic_kernel, grid, dim3(256), shm, s, (const uint8_t*)qI,
                        qI_scale, in_t, w, (const uint8_t*)kI, kI_scale, q_pos, n_entries, Tq, nI,
-                       cI, Nmax, m, scores, sbf);
+                       cI, Nmax, m, scores, sbf, pg);
   }
   return hipGetLastError();
 }

@@ -10,6 +10,29 @@
 
 namespace csa {
 
+// Where entry s of sequence b of one cache series lives.  Dense (table ==
+// nullptr): row b * nrows + s of a [B, nrows] array.  Paged (shuhuayu section
+// 06 / Evidence Ledger Section 3.5.1: blocks of lcm(m, m') tokens, each holding
+// 2^shift entries of the series): slot s & (2^shift - 1) of page
+// table[b * max_blocks + (s >> shift)], pages page_bytes apart.
+struct PageMap {
+  const int32_t* table;
+  int64_t page_bytes;
+  int max_blocks;
+  int shift;
+  __host__ __device__ bool paged() const { return table != nullptr; }
+  // page id of the block holding entry s (paged only)
+  __device__ __forceinline__ int page(int b, int s) const {
+    return table[(int64_t)b * max_blocks + (s >> shift)];
+  }
+  // byte offset of entry s of sequence b from the series base, rows rb bytes
+  __device__ __forceinline__ int64_t off(int b, int s, int nrows, int64_t rb) const {
+    if (table == nullptr) return ((int64_t)b * nrows + s) * rb;
+    return (int64_t)page(b, s) * page_bytes + (int64_t)(s & ((1 << shift) - 1)) * rb;
+  }
+};
+constexpr PageMap kDense = {nullptr, 0, 0, 0};
+
 // prep.hip / compress.hip -------------------------------------------------
 hipError_t launch_prep_rows(const void* x, csa_dtype x_t, int64_t rows, int c,
                             const float* norm_w, float eps, int rope_dims, float rope_theta,
@@ -25,13 +48,14 @@ hipError_t launch_pool(const float* Ca, const float* Za, const float* Cb, const 
                        const float* norm_w, float eps, int rope_dims, float rope_theta,
                        int pos_stride, int pos_offset, void* out, uint8_t* out_scale,
                        csa_dtype out_t, hipStream_t s, const int32_t* entry = nullptr,
-                       int Nmax = 0);
+                       int Nmax = 0, const PageMap& pg = kDense);
 
 // indexer.hip ---------------------------------------------------------------
 hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_t, const float* w,
                           const void* kI, const uint8_t* kI_scale, const int32_t* q_pos,
                           const int32_t* n_entries, int B, int Tq, int nI, int cI, int Nmax,
-                          int m, void* scores, csa_dtype score_t, hipStream_t s);
+                          int m, void* scores, csa_dtype score_t, hipStream_t s,
+                          const PageMap& pg = kDense);
 
 // topk.hip --------------------------------------------------------------------
 // workspace bytes top-k needs (0 for rows of up to 16384 entries)
@@ -64,6 +88,7 @@ struct AttendArgs {
   int B, Tq, nh, c;
   void* out;
   csa_dtype out_t;
+  PageMap pages;             // kv rows: dense [B, Nmax] or paged
 };
 
 // workspace bytes the attention call needs for these host sizes

@@ -44,6 +44,71 @@ def encode_rows(x: torch.Tensor, fmt: int, rows: int, c: int, *, norm_w=None, d_
     return out, sc
 
 
+# ============================================================ paged caches
+@dataclass
+class PagePool:
+    """A hybrid page pool (Evidence Ledger Section 3.5.1; shuhuayu section 06):
+    one page per 128-token block of a sequence, each series of entries in its
+    own section of the page.  ``sections[name] = (byte offset, entries_log2,
+    row bytes)``; ``table[b, j]`` is the page of block j of sequence b."""
+    pool: torch.Tensor
+    table: torch.Tensor
+    page_bytes: int
+    sections: dict
+
+    def base(self, name) -> int:
+        """Device address of slot 0 of page 0 of a series."""
+        return self.pool.data_ptr() + self.sections[name][0]
+
+    def pages(self, name) -> "C.Pages":
+        return C.Pages(self.table, self.sections[name][1], self.page_bytes)
+
+    def _section(self, name):
+        off, lg, rb = self.sections[name]
+        return self.pool[:, off:off + (rb << lg)], 1 << lg, rb
+
+    def scatter(self, name, rows):
+        """Store dense rows (a [B, N, ...] tensor of N rows per sequence, any
+        dtype, read as bytes) as entries 0..N-1 of each sequence's pages."""
+        sec, E, rb = self._section(name)
+        B, nb = self.table.shape
+        r = rows.contiguous().view(torch.uint8).reshape(B, -1, rb)
+        if r.shape[1] < nb * E:
+            pad = torch.full((B, nb * E - r.shape[1], rb), 0xFF, dtype=torch.uint8,
+                             device=r.device)
+            r = torch.cat([r, pad], 1)
+        sec[self.table.reshape(-1).long()] = r.reshape(B * nb, E * rb)
+
+    def gather(self, name, N):
+        """Entries 0..N-1 of every sequence as dense rows [B, N, row bytes]."""
+        sec, E, rb = self._section(name)
+        B, nb = self.table.shape
+        return sec[self.table.reshape(-1).long()].reshape(B, nb * E, rb)[:, :N]
+
+    def clone(self) -> "PagePool":
+        return PagePool(self.pool.clone(), self.table, self.page_bytes, dict(self.sections))
+
+
+def hybrid_pool(B, max_blocks, series, device, seed=0, spare=2) -> PagePool:
+    """A pool of B * max_blocks pages (+ ``spare``), assigned to the blocks in a
+    seeded random order.  ``series``: (name, entries_log2, row bytes) per
+    section, each section 256-byte aligned.  Every byte starts as 0xFF, which
+    no stored row holds (NaN in fp32 / bf16 / e4m3 and e8m0)."""
+    off, sections = 0, {}
+    for name, lg, rb in series:
+        sections[name] = (off, lg, rb)
+        off += ((rb << lg) + 255) // 256 * 256
+    n_pages = B * max_blocks + spare
+    pool = torch.full((n_pages, off), 0xFF, dtype=torch.uint8, device=device)
+    perm = np.random.default_rng(seed).permutation(n_pages)[:B * max_blocks]
+    table = torch.from_numpy(perm.astype(np.int32).reshape(B, max_blocks)).to(device)
+    return PagePool(pool, table, off, sections)
+
+
+def _row_bytes_of(fmt, c, d_r):
+    return {C.F32: 4 * c, C.BF16: 2 * c, C.FP8MIX: (c - d_r) + 2 * d_r, C.MXFP4: c // 2}[fmt]
+
+
 # ============================================================ decode
 @dataclass
 class Decode:
@@ -71,6 +136,7 @@ class Decode:
     ws: Optional[torch.Tensor] = None
     ws_topk: Optional[torch.Tensor] = None
     extra: dict = field(default_factory=dict)
+    pool: Optional[PagePool] = None    # set: the caches live in pages (kv / kI / kI_scale unused)
 
 
 def upload_decode(inp: dict, device="cuda", stream=None) -> Decode:
@@ -115,8 +181,48 @@ def upload_decode(inp: dict, device="cuda", stream=None) -> Decode:
     return d
 
 
+def page_decode(d: Decode, seed=0, drop_dense=False) -> PagePool:
+    """Move a decode batch's caches into a hybrid pool: one page per 128-token
+    block holding 32 CSA main rows, 32 index keys (+ their MXFP4 scales) and 1
+    HCA row.  A CSA workload fills the CSA sections, an HCA workload the HCA
+    section; the other sections belong to the other layer type and stay unused
+    here."""
+    sp = d.spec
+    rb = _row_bytes_of(d.kv_fmt, sp.c, sp.d_r)
+    rbi = _row_bytes_of(d.index_fmt, sp.cI or 128, 0)
+    csa = sp.kind == "decode"
+    series = [("csa_kv", 5, rb), ("kI", 5, rbi)]
+    if csa and d.index_fmt == C.MXFP4:
+        series.append(("kI_scale", 5, (sp.cI or 128) // 32))
+    series.append(("hca_kv", 0, rb))
+    per_block = 32 if csa else 1
+    nb = (d.Nmax + per_block - 1) // per_block
+    pool = hybrid_pool(d.B, nb, series, d.kv.device, seed)
+    if csa:
+        pool.scatter("csa_kv", d.kv)
+        pool.scatter("kI", d.kI)
+        if d.kI_scale is not None:
+            pool.scatter("kI_scale", d.kI_scale)
+    else:
+        pool.scatter("hca_kv", d.kv)
+    d.pool = pool
+    if drop_dense:
+        d.kv = d.kI = d.kI_scale = None
+    return pool
+
+
+def _kv_series(d: Decode):
+    return "csa_kv" if d.spec.kind == "decode" else "hca_kv"
+
+
 def decode_indexer(d: Decode, stream=None):
     sp = d.spec
+    if d.pool is not None:
+        kI, ks = d.pool.base("kI"), (d.pool.base("kI_scale") if d.index_fmt == C.MXFP4 else None)
+        C.indexer_score(d.qI, d.qI_scale, d.index_fmt, d.w, kI, ks, d.index_fmt, d.q_pos,
+                        d.n_entries, d.B, 1, sp.nI, sp.cI, d.Nmax, sp.m, d.scores, d.score_fmt,
+                        stream, pages=d.pool.pages("kI"))
+        return
     C.indexer_score(d.qI, d.qI_scale, d.index_fmt, d.w, d.kI, d.kI_scale, d.index_fmt, d.q_pos,
                     d.n_entries, d.B, 1, sp.nI, sp.cI, d.Nmax, sp.m, d.scores, d.score_fmt, stream)
 
@@ -131,15 +237,18 @@ def decode_attend(d: Decode, idx=None, stream=None):
     sp = d.spec
     qt = C.BF16 if d.q.dtype == torch.bfloat16 else C.F32
     scale = 1.0 / math.sqrt(sp.c)
+    kv, pages = d.kv, None
+    if d.pool is not None:
+        kv, pages = d.pool.base(_kv_series(d)), d.pool.pages(_kv_series(d))
     if sp.kind == "hca_decode":
-        d.ws = C.hca_attend(d.q, qt, d.gamma, EPS, sp.d_r, ROPE_THETA, d.q_pos, d.kv, d.kv_fmt,
+        d.ws = C.hca_attend(d.q, qt, d.gamma, EPS, sp.d_r, ROPE_THETA, d.q_pos, kv, d.kv_fmt,
                             d.Nmax, d.n_entries, sp.m, d.win, sp.n_win, sp.n_win, d.sink, scale,
-                            d.B, 1, sp.nh, sp.c, d.out, C.BF16, d.ws, stream)
+                            d.B, 1, sp.nh, sp.c, d.out, C.BF16, d.ws, stream, pages=pages)
     else:
-        d.ws = C.sparse_mqa_attend(d.q, qt, d.gamma, EPS, sp.d_r, ROPE_THETA, d.q_pos, d.kv,
+        d.ws = C.sparse_mqa_attend(d.q, qt, d.gamma, EPS, sp.d_r, ROPE_THETA, d.q_pos, kv,
                                    d.kv_fmt, d.Nmax, d.idx if idx is None else idx, sp.k, d.win,
                                    sp.n_win, sp.n_win, d.sink, scale, d.B, 1, sp.nh, sp.c, d.out,
-                                   C.BF16, d.ws, stream)
+                                   C.BF16, d.ws, stream, pages=pages)
 
 
 def decode_step(d: Decode, stream=None):
@@ -174,6 +283,9 @@ def decode_chunks(d: Decode, chunks: int):
                          "kI_scale", "w", "scores", "idx", "out"):
                 kw[name] = _batch_slice(kw[name], b0, b1, d.B)
             kw.update(B=int(b1 - b0), ws=None, ws_topk=None, extra={})
+            if d.pool is not None:   # the group's rows of the block table
+                kw["pool"] = PagePool(d.pool.pool, d.pool.table[b0:b1], d.pool.page_bytes,
+                                      d.pool.sections)
             subs.append(Decode(**kw))
         d.extra[key] = subs
     return d.extra[key]

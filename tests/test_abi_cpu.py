@@ -28,7 +28,9 @@ def test_library_loads_and_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"csa_version", "csa_status_string", "csa_prep_rows", "csa_compress",
                           "csa_compress_append", "indexer_score", "topk_select",
-                          "sparse_mqa_attend", "hca_attend"}
+                          "sparse_mqa_attend", "hca_attend", "csa_compress_paged",
+                          "csa_compress_append_paged", "indexer_score_paged",
+                          "sparse_mqa_attend_paged", "hca_attend_paged"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -194,3 +196,78 @@ def test_compress_append_validation_and_workspace():
     assert call(overlap=0) == _lib.ERR_INVALID              # b-series weights without overlap
     assert call(out_t=L.MXFP4) == _lib.ERR_INVALID          # MXFP4 needs a scale array
     assert call() == _lib.ERR_WORKSPACE                     # workspace needed, none given
+
+
+def _pages(max_blocks=64, log2=5, page_bytes=41984, table=D):
+    return ctypes.byref(_lib.CsaPages(table, max_blocks, log2, page_bytes))
+
+
+# a hybrid page of 32 bf16 main rows (1 KiB), 32 bf16 index keys (256 B) and one
+# HCA row: 41,984 bytes
+BAD_PAGES = [
+    dict(table=None),                        # no block table
+    dict(max_blocks=0),
+    dict(log2=17),                           # entries per page out of range
+    dict(page_bytes=41985),                  # not a multiple of 16
+    dict(page_bytes=4096),                   # 32 rows of 1 KiB (or 256 B) do not fit
+    dict(max_blocks=2),                      # 2 blocks x 32 < Nmax
+]
+
+
+@pytest.mark.parametrize("bad", BAD_PAGES)
+def test_paged_calls_check_the_page_descriptor(bad):
+    """Every paged entry point validates the descriptor on the host; a good one
+    passes (workspace queries, or empty batches that launch nothing)."""
+    lib = L.lib()
+    Nmax = 1024
+
+    def attend(pages, kv=D):
+        need = ctypes.c_size_t(0)
+        return lib.sparse_mqa_attend_paged(D, L.BF16, None, 1e-6, 64, 1e4, D, kv, L.BF16, Nmax,
+                                           pages, D, 512, D, 128, 128, D, 0.04, 4, 1, 64, 512, D,
+                                           L.BF16, None, ctypes.byref(need), None)
+
+    def hca(pages):
+        need = ctypes.c_size_t(0)
+        return lib.hca_attend_paged(D, L.BF16, None, 1e-6, 64, 1e4, D, D, L.BF16, Nmax, pages, D,
+                                    128, D, 128, 128, D, 0.04, 4, 1, 64, 512, D, L.BF16, None,
+                                    ctypes.byref(need), None)
+
+    def index(pages, kI=D):
+        return lib.indexer_score_paged(D, None, L.BF16, D, kI, None, L.BF16, pages, D, D, 0, 1,
+                                       64, 128, Nmax, 4, D, L.F32, None)
+
+    def compress(pages):
+        need = ctypes.c_size_t(0)
+        return lib.csa_compress_paged(D, L.BF16, 1, 4 * Nmax, 256, D, D, D, D, D, D, 4, 1, 512,
+                                      D, 1e-6, 64, 1e4, 4, 0, D, None, L.BF16, pages, None,
+                                      ctypes.byref(need), None)
+
+    def append(pages):
+        need = ctypes.c_size_t(0)
+        return lib.csa_compress_append_paged(D, L.BF16, 4, 256, D, D, D, D, D, D, 4, 1, 512, D,
+                                             1e-6, 64, 1e4, 4, 0, D, D, None, L.BF16, Nmax, pages,
+                                             None, ctypes.byref(need), None)
+
+    calls = [attend, index, compress, append]
+    for f in calls:
+        assert f(_pages()) == _lib.OK, f.__name__
+        assert f(None) == _lib.ERR_INVALID, f.__name__
+        assert f(_pages(**bad)) == _lib.ERR_INVALID, (f.__name__, bad)
+    # HCA rows: one entry per page
+    assert hca(_pages(log2=0, max_blocks=Nmax)) == _lib.OK
+    assert hca(_pages(log2=0, max_blocks=Nmax - 1)) == _lib.ERR_INVALID
+    # series bases must be 16-byte aligned
+    assert attend(_pages(), kv=D + 8) == _lib.ERR_INVALID
+    assert index(_pages(), kI=D + 4) == _lib.ERR_INVALID
+
+
+def test_paged_compress_needs_the_same_workspace_as_dense():
+    lib = L.lib()
+    dense, paged = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    args = (D, L.BF16, 2, 4096, 256, D, D, D, D, D, D, 4, 1, 512, D, 1e-6, 64, 1e4, 4, 0, D, None,
+            L.BF16)
+    assert lib.csa_compress(*args, None, ctypes.byref(dense), None) == _lib.OK
+    assert lib.csa_compress_paged(*args, _pages(max_blocks=32), None, ctypes.byref(paged),
+                                  None) == _lib.OK
+    assert dense.value == paged.value > 0
