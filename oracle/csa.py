@@ -38,6 +38,13 @@ Readings taken where the pages are silent (each is a parameter where cheap):
 * The attention logit is tau * (q . x) with tau = 1/sqrt(c); the sink enters
   the denominator as exp(z'_h) with no scaling; x serves as both K and V,
   including its RoPE channels, and the output is rotated back by -q.
+* Grouped output projection: group j takes the consecutive heads
+  j*nh/g .. (j+1)*nh/g - 1, their rotated-back outputs concatenated head by
+  head; each group is projected to d_g by its own matrix and the g results,
+  concatenated in group order, are projected to d.  No nonlinearity sits
+  between the two products.  Weights follow the linear-layer convention
+  [out, in].  The activation u between them may be rounded (bf16 in the
+  kernels), passed in as ``round_u``.
 """
 from __future__ import annotations
 
@@ -314,6 +321,43 @@ def dense_attend(q_raw, gamma_q, eps, d_r, theta, q_pos, kv, m_prime, win, n_win
         X = gather_rows(kv, np.arange(nv), win, int(p), n_win, win_len)
         out[t] = attend_query(q_raw[t], gamma_q, eps, d_r, theta, int(p), X, sink, tau)
     return out
+
+
+# --------------------------------------------------------------------------
+# grouped output projection (Evidence Ledger, Section 2.3.1: n_h heads -> g
+# groups -> d_g intermediates -> d; shuhuayu page section 03: outputs are
+# rotated back before the grouped projection, configuration table: output
+# groups / rank per group)
+# --------------------------------------------------------------------------
+
+
+def grouped_out_proj(o, W_a, W_b, round_u=None):
+    """Grouped output projection of attention outputs.
+
+    o    [R, nh, c]  per query row, the heads' outputs (already rotated by -q)
+    W_a  [g, d_g, nh/g * c]  group j's projection (linear convention [out, in])
+    W_b  [d, g * d_g]        the output projection
+
+    u_j = concat(o[h] for h in group j) . W_a[j]^T   (R x d_g)
+    y   = [u_0 | u_1 | ... | u_{g-1}] . W_b^T         (R x d)
+    Returns (y, u) in fp64; ``round_u`` (if given) is applied to u before the
+    second product."""
+    o = np.asarray(o, dtype=np.float64)
+    W_a = np.asarray(W_a, dtype=np.float64)
+    W_b = np.asarray(W_b, dtype=np.float64)
+    R, nh, c = o.shape
+    g, d_g, K1 = W_a.shape
+    if nh % g or K1 != nh // g * c or W_b.shape[1] != g * d_g:
+        raise ValueError("inconsistent grouped projection shapes")
+    hpg = nh // g
+    u = np.empty((R, g, d_g))
+    for j in range(g):
+        oj = o[:, j * hpg:(j + 1) * hpg, :].reshape(R, K1)   # heads of group j, head-major
+        u[:, j, :] = oj @ W_a[j].T
+    u = u.reshape(R, g * d_g)
+    if round_u is not None:
+        u = np.asarray(round_u(u), dtype=np.float64)
+    return u @ W_b.T, u
 
 
 # --------------------------------------------------------------------------

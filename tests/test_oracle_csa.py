@@ -390,3 +390,60 @@ def test_window_includes_current_token_only_at_q0():
     ring = rng.standard_normal((128, 4))
     rows = O.gather_rows(np.zeros((1, 4)), [-1], ring, 130, 128, 128)
     assert rows.shape[0] == 128 and np.array_equal(rows[-1], ring[2])
+
+
+# =================================================================== grouped output projection
+def _oproj_case(rng, R=3, nh=8, c=6, g=4, d_g=5, d=7):
+    o = rng.standard_normal((R, nh, c))
+    W_a = rng.standard_normal((g, d_g, nh // g * c))
+    W_b = rng.standard_normal((d, g * d_g))
+    return o, W_a, W_b
+
+
+def test_grouped_out_proj_is_a_block_diagonal_map():
+    """The grouped projection is the block-diagonal matrix of the group
+    projections (scipy's block_diag) applied to the flattened heads, then W_b:
+    a transposed operand, a wrong flattening or a wrong group order fails."""
+    from scipy.linalg import block_diag
+    rng = np.random.default_rng(71)
+    for shape in [dict(), dict(nh=6, g=3, c=4, d_g=2, d=5), dict(nh=4, g=1, c=3, d_g=6, d=2),
+                  dict(nh=4, g=4, c=2, d_g=3, d=3)]:
+        o, W_a, W_b = _oproj_case(rng, **shape)
+        y, u = O.grouped_out_proj(o, W_a, W_b)
+        R = o.shape[0]
+        BD = block_diag(*W_a)                       # [g*d_g, nh*c]
+        np.testing.assert_allclose(u, o.reshape(R, -1) @ BD.T, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(y, (o.reshape(R, -1) @ BD.T) @ W_b.T, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_out_proj_groups_are_consecutive_heads():
+    """Perturbing head h changes only u's block h // (nh/g)."""
+    rng = np.random.default_rng(72)
+    o, W_a, W_b = _oproj_case(rng)
+    nh, g, d_g = o.shape[1], W_a.shape[0], W_a.shape[1]
+    _, u0 = O.grouped_out_proj(o, W_a, W_b)
+    for h in range(nh):
+        o2 = o.copy()
+        o2[:, h, :] += 1.0
+        _, u2 = O.grouped_out_proj(o2, W_a, W_b)
+        changed = [bool(np.any(u2[:, j * d_g:(j + 1) * d_g] != u0[:, j * d_g:(j + 1) * d_g]))
+                   for j in range(g)]
+        assert changed == [j == h // (nh // g) for j in range(g)], h
+
+
+def test_grouped_out_proj_rounding_hook_and_shapes():
+    """round_u acts on u only (bf16 keeps 8 significant bits, so rounding moves
+    each u by at most 2^-8 |u| and y by at most 2^-8 |u| . |W_b|);
+    inconsistent shapes are rejected."""
+    import torch
+    rng = np.random.default_rng(73)
+    o, W_a, W_b = _oproj_case(rng, R=4, nh=8, c=16, g=2, d_g=32, d=9)
+    y, u = O.grouped_out_proj(o, W_a, W_b)
+    bf = lambda x: torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    yb, ub = O.grouped_out_proj(o, W_a, W_b, round_u=bf)
+    assert np.all(np.abs(ub - u) <= 2.0 ** -8 * np.abs(u))
+    assert np.all(np.abs(yb - y) <= 2.0 ** -8 * (np.abs(u) @ np.abs(W_b).T) + 1e-12)
+    with pytest.raises(ValueError):
+        O.grouped_out_proj(o, W_a[:, :, :-1], W_b)
+    with pytest.raises(ValueError):
+        O.grouped_out_proj(o[:, :7], W_a, W_b)
