@@ -247,6 +247,91 @@ def run_decode(args, torch, I, G):
     return res, inp
 
 
+# ------------------------------------------------------------------ output projection
+# the Flash shape of the configuration table: 64 heads x 512, 8 groups of rank
+# 1024, hidden 4096; decode = one step's 32 query rows, prefill = 32K rows
+OPROJ = dict(oproj_decode=32, oproj_prefill=32768)
+
+
+def run_oproj(args, torch):
+    import long_context_sparse_10_amd as L
+    R, nh, c, g, d_g, d = OPROJ[args.config], 64, 512, 8, 1024, 4096
+    K1, Ku = nh // g * c, g * d_g
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev).manual_seed(1007)
+    bf = torch.bfloat16
+    o = torch.randn(R, nh, c, generator=gen, device=dev).to(bf)
+    # weight copies rotated so the 128 MiB of weights do not stay in the
+    # 256 MiB Infinity Cache between calls (decode)
+    ncopy = 3 if R <= 64 else 1
+    Ws = [((torch.randn(g, d_g, K1, generator=gen, device=dev) / math.sqrt(K1)).to(bf),
+           (torch.randn(d, Ku, generator=gen, device=dev) / math.sqrt(Ku)).to(bf))
+          for _ in range(ncopy)]
+    y = torch.empty(R, d, dtype=bf, device=dev)
+    stream = torch.cuda.Stream()
+    ws = None
+    with torch.cuda.stream(stream):
+        for i in range(max(args.warmup, ncopy)):
+            Wa, Wb = Ws[i % ncopy]
+            ws = L.grouped_out_proj(o, L.BF16, R, nh, c, g, d_g, Wa, Wb, d, y, L.BF16, ws, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(args.steps):
+            Wa, Wb = Ws[i % ncopy]
+            L.grouped_out_proj(o, L.BF16, R, nh, c, g, d_g, Wa, Wb, d, y, L.BF16, ws, stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    call_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    ms = elapsed / args.steps * 1e3
+    flops = 2.0 * R * (nh * c * d_g + Ku * d)
+    # algorithmic bytes: both weight matrices, o, y, and u written and read once
+    nbytes = 2 * (g * d_g * K1 + d * Ku + R * nh * c + R * d + 2 * R * Ku)
+    cfg = dict(workload=args.config, rows=R, heads=nh, head_dim=c, groups=g, rank_per_group=d_g,
+               hidden=d, weight_copies=ncopy)
+    res = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=ms,
+               higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+               data="synthetic", config=cfg,
+               step=dict(call_us=call_us, kernels="u = per-group o.W_a^T, then y = u.W_b^T"))
+    if R <= 64:
+        gbs = nbytes / (call_us * 1e-6) / 1e9
+        res.update(value=R / (ms * 1e-3), unit="query-tokens/s",
+                   roofline=dict(bound="hbm", kernel="grouped_out_proj", achieved=gbs,
+                                 peak=HBM_PEAK_GBS, unit="GB/s", frac=gbs / HBM_PEAK_GBS,
+                                 traffic=None, algorithmic_bytes_per_launch=nbytes,
+                                 avg_launch_us=call_us))
+    else:
+        tf = flops / (call_us * 1e-6) / 1e12
+        res.update(value=flops / (ms * 1e-3) / 1e12, unit="TFLOP/s",
+                   roofline=dict(bound="mfma", kernel="grouped_out_proj", achieved=tf,
+                                 peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=tf / BF16_PEAK_TFLOPS,
+                                 traffic=None, algorithmic_flops_per_launch=flops,
+                                 avg_launch_us=call_us))
+    return res, (o, Ws[0], R, nh, c, g, d_g, d)
+
+
+def cpu_baseline_oproj(case, budget_s=10.0):
+    """The oracle's grouped projection on a bounded sample of rows."""
+    from oracle import csa as O
+    o, (Wa, Wb), R, nh, c, g, d_g, d = case
+    rows = min(R, 32)
+    oo = o[:rows].float().cpu().numpy()
+    Wa_, Wb_ = Wa.float().cpu().numpy(), Wb.float().cpu().numpy()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        O.grouped_out_proj(oo, Wa_, Wb_)
+        n += rows
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="query-tokens/s", cores=blas_threads(), kind="oracle",
+                sample=f"{n} rows ({rows} per call) of the same shape, fp64 numpy, {dt:.1f} s")
+
+
 # ------------------------------------------------------------------ prefill bench
 def run_prefill(args, torch, I, G):
     sp = I.CONFIGS[args.config]
@@ -346,7 +431,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_64k",
                     choices=["decode_64k", "hca_decode_1m", "decode_1m_fp4", "prefill_32k",
-                             "prefill_32k_mxfp4"])
+                             "prefill_32k_mxfp4", "oproj_decode", "oproj_prefill"])
     ap.add_argument("--copies", type=int, default=6, help="cache copies rotated (cold cache)")
     ap.add_argument("--graph", action="store_true", help="decode: replay each step as a HIP graph")
     ap.add_argument("--chunks", type=int, default=1,
@@ -368,6 +453,12 @@ def main():
         return
     import csa_inputs as I
     from long_context_sparse_10_amd import pipeline as G
+    if args.config in OPROJ:
+        res, case = run_oproj(args, torch)
+        res["roofline"]["traffic"] = kernel_traffic(args.config)
+        res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_oproj(case)
+        print(json.dumps(res), flush=True)
+        return
     if args.config.startswith("prefill"):
         args.copies = 1
         res, inp = run_prefill(args, torch, I, G)

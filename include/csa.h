@@ -263,6 +263,31 @@ csa_status hca_attend(const void* q, csa_dtype q_t, const float* q_norm_w, float
                       void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /*
+ * grouped_out_proj -- the grouped output projection (Evidence Ledger Section
+ * 2.3.1: n_h heads -> g groups -> d_g intermediates -> d; shuhuayu section 03:
+ * the attention outputs are rotated back by -q before it -- the attention
+ * calls' epilogue does that -- and its configuration table: 8 groups of rank
+ * 1024 for 64 heads x 512, 16 for 128 heads):
+ *
+ *   u[r, j*d_g + e] = sum_k o[r, j*K1 + k] * W_a[j, e, k],   K1 = nh/g * c
+ *   y[r, n]         = sum_k u[r, k] * W_b[n, k]               k < g * d_g
+ *
+ *  o    [R, nh, c] in t (attention output rows, R = B * Tq); group j is heads
+ *       j*nh/g .. (j+1)*nh/g - 1, concatenated head by head.
+ *  W_a  [g, d_g, K1] and W_b [d, g*d_g] in t (linear-layer [out, in] layout).
+ *  t    CSA_BF16 (matrix cores, fp32 accumulation; u is rounded to bf16
+ *       between the products) or CSA_F32 (fp32 throughout).
+ *  y    [R, d] in y_t (CSA_F32, or CSA_BF16 rounded RNE).
+ *  ws   u (R * g * d_g elements of t) and, for R <= 64, fp32 partial sums of
+ *       the K-slices (workspace protocol).
+ *  CSA_BF16 needs K1 and g*d_g multiples of 32 and 16-byte aligned o, W_a,
+ *  W_b, y and ws; nh must be a multiple of g.  Else CSA_ERR_INVALID.
+ */
+csa_status grouped_out_proj(const void* o, csa_dtype t, int R, int nh, int c, int g, int d_g,
+                            const void* W_a, const void* W_b, int d, void* y, csa_dtype y_t,
+                            void* ws, size_t* ws_bytes, hipStream_t stream);
+
+/*
  * Paged caches (Evidence Ledger Section 3.5.1; shuhuayu section 06 "Hybrid
  * attention creates a hybrid cache"): compressed entries live in fixed-size
  * blocks covering lcm(m, m') tokens, so one block of 128 tokens holds 32 CSA

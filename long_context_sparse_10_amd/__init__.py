@@ -3,14 +3,15 @@ and its thin Python binding.
 
 The five calls of the path -- ``csa_compress``, ``indexer_score``,
 ``topk_select``, ``sparse_mqa_attend``, ``hca_attend`` -- plus the row encoder
-``csa_prep_rows`` and the decode-time ``csa_compress_append`` are re-exported
+``csa_prep_rows``, the decode-time ``csa_compress_append`` and the
+``grouped_out_proj`` that follows attention are re-exported
 from :mod:`._lib` with torch tensors in place of device pointers.  The cache
 calls take ``pages=Pages(...)`` for caches held in a paged pool (the
 ``*_paged`` entry points).  See ``include/csa.h`` for the contract of each call.
 """
 from ._lib import (  # noqa: F401
     BF16, F32, FP8MIX, MXFP4, CsaError, LIB_PATH, Pages, csa_compress, csa_compress_append,
-    csa_prep_rows, hca_attend,
+    csa_prep_rows, grouped_out_proj, hca_attend,
     indexer_score, lib, sparse_mqa_attend, status_string, topk_select, version,
 )
 

@@ -48,6 +48,8 @@ SIGNATURES = {
                           _psz, _vp],
     "hca_attend": [_vp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32,
                    _i32, _vp, _f32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _psz, _vp],
+    "grouped_out_proj": [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _i32, _vp,
+                         _psz, _vp],
     "csa_compress_paged": [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                            _i32, _vp, _f32, _i32, _f32, _i32, _i32, _vp, _vp, _i32, _pp, _vp,
                            _psz, _vp],
@@ -256,4 +258,16 @@ def hca_attend(q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, kv_t, Nm
         return L.hca_attend(*head, *tail, wp, szp, sid)
     st, ws = _workspace(call, q.device, ws)
     _check("hca_attend_paged" if ps is not None else "hca_attend", st)
+    return ws
+
+
+def grouped_out_proj(o, t, R, nh, c, g, d_g, W_a, W_b, d, y, y_t, ws=None, stream=None):
+    L = lib()
+    sid = _s(stream)
+
+    def call(wp, szp):
+        return L.grouped_out_proj(_p(o), t, R, nh, c, g, d_g, _p(W_a), _p(W_b), d, _p(y), y_t, wp,
+                                  szp, sid)
+    st, ws = _workspace(call, o.device, ws)
+    _check("grouped_out_proj", st)
     return ws

@@ -326,6 +326,28 @@ csa_status topk_select(const void* scores, csa_dtype score_t, const int32_t* q_p
                                    stream));
 }
 
+csa_status grouped_out_proj(const void* o, csa_dtype t, int R, int nh, int c, int g, int d_g,
+                            const void* W_a, const void* W_b, int d, void* y, csa_dtype y_t,
+                            void* ws, size_t* ws_bytes, hipStream_t stream) {
+  if (o == nullptr || W_a == nullptr || W_b == nullptr || y == nullptr) return CSA_ERR_INVALID;
+  if (R < 0 || nh <= 0 || c <= 0 || g <= 0 || d_g <= 0 || d <= 0 || nh % g != 0)
+    return CSA_ERR_INVALID;
+  if (!is_f32_bf16(t) || !is_f32_bf16(y_t)) return CSA_ERR_UNSUPPORTED;
+  const int64_t K1 = (int64_t)nh / g * c, Ku = (int64_t)g * d_g;
+  if (K1 > INT_MAX || Ku > INT_MAX || (int64_t)R * nh * c > (1ll << 40) || R > (1 << 24))
+    return CSA_ERR_INVALID;
+  if (t == CSA_BF16) {
+    if (K1 % 32 != 0 || Ku % 32 != 0) return CSA_ERR_INVALID;
+    if ((uintptr_t)o % 16 || (uintptr_t)W_a % 16 || (uintptr_t)W_b % 16 || (uintptr_t)y % 16 ||
+        (uintptr_t)ws % 16)
+      return CSA_ERR_INVALID;
+  }
+  csa_status st;
+  if (ws_query(ws, ws_bytes, oproj_workspace(R, nh, c, g, d_g, d, t), &st)) return st;
+  if (R == 0) return CSA_OK;
+  return launch_status(launch_oproj(o, t, R, nh, c, g, d_g, W_a, W_b, d, y, y_t, ws, stream));
+}
+
 static csa_status attend_common(AttendArgs& a, const csa_pages* pages, void* ws,
                                 size_t* ws_bytes, hipStream_t stream) {
   a.pages = kDense;

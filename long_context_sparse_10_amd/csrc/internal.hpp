@@ -64,6 +64,12 @@ hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_p
                        const int32_t* n_entries, int B, int Tq, int Nmax, int m, int k,
                        int32_t* idx, void* ws, hipStream_t s);
 
+// oproj.hip --------------------------------------------------------------------
+size_t oproj_workspace(int R, int nh, int c, int g, int d_g, int d, csa_dtype t);
+hipError_t launch_oproj(const void* o, csa_dtype t, int R, int nh, int c, int g, int d_g,
+                        const void* W_a, const void* W_b, int d, void* y, csa_dtype y_t, void* ws,
+                        hipStream_t s);
+
 // attend.hip -------------------------------------------------------------------
 struct AttendArgs {
   const void* q;

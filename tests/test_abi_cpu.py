@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
                           "csa_compress_append", "indexer_score", "topk_select",
                           "sparse_mqa_attend", "hca_attend", "csa_compress_paged",
                           "csa_compress_append_paged", "indexer_score_paged",
-                          "sparse_mqa_attend_paged", "hca_attend_paged"}
+                          "sparse_mqa_attend_paged", "hca_attend_paged", "grouped_out_proj"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -271,3 +271,24 @@ def test_paged_compress_needs_the_same_workspace_as_dense():
     assert lib.csa_compress_paged(*args, _pages(max_blocks=32), None, ctypes.byref(paged),
                                   None) == _lib.OK
     assert dense.value == paged.value > 0
+
+
+def test_grouped_out_proj_validation_and_workspace():
+    f = L.lib().grouped_out_proj
+
+    def call(o=D, t=L.BF16, R=32, nh=64, c=512, g=8, d_g=1024, Wa=D, Wb=D, d=4096, y=D,
+             y_t=L.BF16, ws=None, szp=None):
+        return f(o, t, R, nh, c, g, d_g, Wa, Wb, d, y, y_t, ws, szp, None)
+    need = ctypes.c_size_t(0)
+    assert call(szp=ctypes.byref(need)) == _lib.OK
+    # u in bf16, then fp32 K-slice partials (4 slices x 32 x 8192, or 8 x 32 x 4096)
+    assert need.value == 32 * 8 * 1024 * 2 + 8 * 32 * 4096 * 4
+    assert call(t=L.F32, szp=ctypes.byref(need)) == _lib.OK
+    assert need.value == 32 * 8 * 1024 * 4                      # u in fp32 only
+    assert call(nh=60) == _lib.ERR_INVALID                      # heads not a multiple of g
+    assert call(c=6, szp=ctypes.byref(need)) == _lib.ERR_INVALID    # bf16 K1 = 48, not a multiple of 32
+    assert call(Wa=None) == _lib.ERR_INVALID
+    assert call(y=D + 8) == _lib.ERR_INVALID                    # 16-byte alignment
+    assert call(t=L.MXFP4) == _lib.ERR_UNSUPPORTED
+    assert call(R=0, szp=ctypes.byref(need)) == _lib.OK and need.value == 0
+    assert call() == _lib.ERR_WORKSPACE
