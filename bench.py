@@ -40,14 +40,27 @@ METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP
 # of known size (--copy-probe).  An entry holds for the kernel source it was
 # taken on (sha256 of the .hip file); after any change it reports null.
 TRAFFIC = {
-    "decode_64k": dict(src="indexer.hip", sha256="cf0bb6345b2835efd0cb8312177db31e9c68837b777a8ebb0c8ad990dea3ba19",
-                fetch_kib=67667.0, write_kib=2048.4, fetch_scale=1.9998, write_scale=1.0),
-    "hca_decode_1m": dict(src="attend.hip", sha256="5b4d4b06a72f3d4197e2e30bced149a626c0df3d59d0b90bcc580457e96529c4",
-                fetch_kib=80743.0, write_kib=18560.3, fetch_scale=1.9998, write_scale=1.0),
-    "decode_1m_fp4": dict(src="indexer.hip", sha256="cf0bb6345b2835efd0cb8312177db31e9c68837b777a8ebb0c8ad990dea3ba19",
-                fetch_kib=69890.2, write_kib=4096.8, fetch_scale=1.9998, write_scale=1.0),
-    "prefill_32k": dict(src="attend.hip", sha256="5b4d4b06a72f3d4197e2e30bced149a626c0df3d59d0b90bcc580457e96529c4",
-                fetch_kib=3600826.6, write_kib=2222392.2, fetch_scale=1.9998, write_scale=1.0),
+    "decode_64k": dict(src="indexer.hip", sha256="213e05c5c94a7cbb737f73159c9137fecde78845a8e2d6980bc8c315f6a8e8ac",
+                fetch_kib=67679.0, write_kib=2048.9, fetch_scale=1.9998,
+                write_scale=1.0),
+    "hca_decode_1m": dict(src="attend.hip", sha256="ee655a444067cb9d95284cd40f59c81b3355a772a183c3e8df29436863cccf48",
+                fetch_kib=76325.6, write_kib=18560.0, fetch_scale=1.9998,
+                write_scale=1.0),
+    "decode_1m_fp4": dict(src="indexer.hip", sha256="213e05c5c94a7cbb737f73159c9137fecde78845a8e2d6980bc8c315f6a8e8ac",
+                fetch_kib=69948.9, write_kib=4096.1, fetch_scale=1.9998,
+                write_scale=1.0),
+    "prefill_32k": dict(src="attend.hip", sha256="ee655a444067cb9d95284cd40f59c81b3355a772a183c3e8df29436863cccf48",
+                fetch_kib=3361022.1, write_kib=2222125.1, fetch_scale=1.9998,
+                write_scale=1.0),
+    "prefill_32k_mxfp4": dict(src="attend.hip", sha256="ee655a444067cb9d95284cd40f59c81b3355a772a183c3e8df29436863cccf48",
+                fetch_kib=3364576.3, write_kib=2223454.5, fetch_scale=1.9998,
+                write_scale=1.0),
+    "oproj_decode": dict(src="oproj.hip", sha256="06319b9ca96d03bb318e747f4f43e1700e84cf3614483fca35e959f5e807318e",
+                fetch_kib=80952.1, write_kib=8969.2, fetch_scale=1.9998,
+                write_scale=1.0),
+    "oproj_prefill": dict(src="oproj.hip", sha256="06319b9ca96d03bb318e747f4f43e1700e84cf3614483fca35e959f5e807318e",
+                fetch_kib=12924029.9, write_kib=952182.6, fetch_scale=1.9998,
+                write_scale=1.0),
 }
 
 
