@@ -219,3 +219,86 @@ def test_paged_prefill_shaped_indexer_vs_oracle():
             assert np.all(np.isnan(S[b, t, nv:])), (b, t)
             worst = max(worst, float(np.abs(S[b, t, :nv] - want).max()))
     report("paged indexer query rows", max_err=worst)
+
+
+def test_paged_decode_loop_with_appends():
+    """A serving loop on one sequence (prefill_32k shapes, 2,048 tokens): the
+    first 1,027 tokens are prefilled into a hybrid page pool; then 13 decode
+    steps each run indexer -> top-k -> attention on the paged caches, and every
+    block that completes appends its main entry and index key into the pages
+    first.  Appended rows equal the full compressor's rows bit for bit; each
+    step's scores, selection and output match the oracle."""
+    from tests.gpu_util import score_error_bound
+    from tests.test_gpu_full import check_topk
+    d = dev()
+    sp = I.CONFIGS["prefill_32k"]
+    T = 2048
+    inp = I.prefill_inputs(sp, T=T)
+    p = G.upload_prefill(inp, d)
+    G.prefill_compress(p)                     # dense rows of all T tokens: the reference
+    torch.cuda.synchronize()
+    m, n_all = sp.m, T // sp.m
+    T0, steps = 1027, 13
+    rb = L.row_bytes(L.BF16, sp.c, sp.d_r)
+    series = [("csa_kv", 5, rb), ("kI", 5, 2 * sp.cI), ("hca_kv", 0, rb)]
+    pool = G.hybrid_pool(1, (n_all + 31) // 32, series, d, seed=11)
+    n0 = T0 // m
+    pool.scatter("csa_kv", p.kv.view(1, n_all, rb)[:, :n0])
+    pool.scatter("kI", p.kI.view(1, n_all, 2 * sp.cI)[:, :n0])
+    caches = OP.prefill_caches(inp)
+    W = p.W
+    Nmax = n_all
+    scale = 1.0 / math.sqrt(sp.c)
+    scores = torch.empty(1, 1, Nmax, dtype=torch.float32, device=d)
+    idx = torch.empty(1, 1, sp.k, dtype=torch.int32, device=d)
+    out = torch.empty(1, 1, sp.nh, sp.c, dtype=torch.bfloat16, device=d)
+    ws = ws_a = ws_i = None
+    appended, worst, exact = [], 0.0, 0
+    for q in range(T0, T0 + steps):
+        if (q + 1) % m == 0:                  # block i completes with token q: append entry i
+            i = (q + 1) // m - 1
+            tail = p.H[m * i - m: m * i + m].reshape(1, 2 * m, sp.d)
+            e = torch.tensor([i], dtype=torch.int32, device=d)
+            ws_a = L.csa_compress_append(tail, L.BF16, 1, sp.d, W["W_kv_a"], W["W_z_a"], W["W_kv_b"],
+                                         W["W_z_b"], W["bias_a"], W["bias_b"], m, 1, sp.c, p.gamma,
+                                         G.EPS, sp.d_r, G.ROPE_THETA, m, 0, e, pool.base("csa_kv"),
+                                         None, L.BF16, Nmax, ws_a, pages=pool.pages("csa_kv"))
+            ws_i = L.csa_compress_append(tail, L.BF16, 1, sp.d, W["WI_kv_a"], W["WI_z_a"],
+                                         W["WI_kv_b"], W["WI_z_b"], W["biasI_a"], W["biasI_b"], m, 1,
+                                         sp.cI, None, G.EPS, 0, G.ROPE_THETA, m, 0, e,
+                                         pool.base("kI"), None, L.BF16, Nmax, ws_i,
+                                         pages=pool.pages("kI"))
+            appended.append(i)
+        qp = torch.tensor([[q]], dtype=torch.int32, device=d)
+        nv_dev = torch.tensor([(q + 1) // m], dtype=torch.int32, device=d)
+        L.indexer_score(p.qI[q:q + 1].reshape(1, 1, sp.nI, sp.cI), None, L.BF16,
+                        p.w[q:q + 1].reshape(1, 1, sp.nI), pool.base("kI"), None, L.BF16, qp, nv_dev,
+                        1, 1, sp.nI, sp.cI, Nmax, m, scores, L.F32, pages=pool.pages("kI"))
+        L.topk_select(scores, L.F32, qp, nv_dev, 1, 1, Nmax, m, sp.k, idx)
+        ws = L.sparse_mqa_attend(p.q[q:q + 1].reshape(1, 1, sp.nh, sp.c), L.BF16, p.gamma, G.EPS,
+                                 sp.d_r, G.ROPE_THETA, qp, pool.base("csa_kv"), L.BF16, Nmax, idx,
+                                 sp.k, p.win, T, sp.n_win, p.sink, scale, 1, 1, sp.nh, sp.c, out,
+                                 L.BF16, ws, pages=pool.pages("csa_kv"))
+        torch.cuda.synchronize()
+        (ref,) = OP.prefill_reference(inp, caches, [q])
+        nv = ref["n_vis"]
+        srow = scores[0, 0, :nv].double().cpu().numpy()
+        bound = score_error_bound(inp["qI"][q], inp["w"][q], caches["kI"], nv)
+        kb = score_error_bound(inp["qI"][q], inp["w"][q], caches["kI_exact"], nv, rel=2 ** -8)
+        assert np.all(np.abs(srow - ref["scores"]) <= bound + kb + 1e-6), q
+        got_idx = idx[0, 0].cpu().numpy()
+        exact += check_topk(got_idx, ref["scores"], nv, sp.k, float((bound + kb).max()))
+        X = O.gather_rows(caches["kv"], got_idx, caches["win"], q, sp.n_win, T)
+        want = O.attend_query(inp["q"][q], None, G.EPS, sp.d_r, G.ROPE_THETA, q, X, inp["sink"], scale)
+        err = float(np.abs(out[0, 0].double().cpu().numpy() - want).max())
+        worst = max(worst, err)
+        assert err <= 2e-2, (q, err)
+    # the appended entries are the full compressor's rows
+    kv = pool.gather("csa_kv", n_all)[0]
+    kI = pool.gather("kI", n_all)[0]
+    for i in appended:
+        assert torch.equal(kv[i], p.kv.view(n_all, rb)[i]), i
+        assert torch.equal(kI[i], p.kI.view(n_all, 2 * sp.cI)[i]), i
+    assert appended == [256, 257, 258, 259]
+    report("paged decode loop", steps=steps, appended=appended, idx_exact=exact,
+           max_abs_vs_oracle=worst)
