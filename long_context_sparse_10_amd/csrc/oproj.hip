@@ -19,8 +19,10 @@
 //    16-column tile would move twice the weights' bytes; per 128-column tile
 //    it moves an eighth of them.  The K-slices' fp32 partial sums are added in
 //    slice order by oproj_reduce_kernel: deterministic.
-//  * many rows (prefill): oproj_tiled_kernel, 128 x 128 output tiles staged
-//    through LDS, v_mfma_f32_32x32x16_bf16, MFMA-bound.
+//  * many rows (prefill): oproj_tiled_kernel, 256 x 128 output tiles through a
+//    double-buffered LDS stage, 128 x 64 per wave on v_mfma_f32_32x32x16_bf16
+//    (24 B of LDS reads per MFMA cycle per wave, against 32 for 64 x 64), row
+//    panels kept on one XCD.
 //  * fp32 operands: oproj_generic_kernel, one thread per output (small cases).
 #include "common.hpp"
 #include "internal.hpp"
@@ -128,59 +130,93 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(const float* __restri
 }
 
 // =============================================================== many rows
-constexpr int OT_M = 128, OT_N = 128, OT_K = 32, OT_LD = OT_K + 8;
+constexpr int OT_M = 256, OT_N = 128, OT_K = 32, OT_LD = OT_K + 8;
 
-__global__ __launch_bounds__(256) void oproj_tiled_kernel(
+// C tile 256 x 128 per 256-thread block; wave w owns rows 128 (w / 2) .. +127
+// and columns 64 (w % 2) .. +63 as 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.
+// K advances by 32 through a double-buffered LDS stage: the next slice is read
+// from global memory into registers while the current one is multiplied, then
+// written to the other buffer; one barrier per step.  Blocks are ordered for
+// the XCDs: every column tile of row panel mt runs on XCD mt % 8, so the panel
+// of A is fetched into one L2.
+__global__ __launch_bounds__(256, 2) void oproj_tiled_kernel(
     const uint16_t* __restrict__ A, int64_t lda, int64_t a_goff, const uint16_t* __restrict__ W,
     int64_t w_gstride, void* __restrict__ C, int64_t ldc, int64_t c_goff, int c_bf16, int M, int N,
     int K) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[OT_M][OT_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[OT_N][OT_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][OT_M][OT_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][OT_N][OT_LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = blockIdx.z;
-  const int m0 = blockIdx.y * OT_M, n0 = blockIdx.x * OT_N;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int nN = (N + OT_N - 1) / OT_N, nM = (M + OT_M - 1) / OT_M;
+  const int per_grp = (nM + 7) / 8 * 8 * nN;
+  const int grp = blockIdx.x / per_grp, L = blockIdx.x % per_grp;
+  const int mt = (L / 8 / nN) * 8 + (L & 7), nt = (L / 8) % nN;
+  if (mt >= nM) return;
+  const int m0 = mt * OT_M, n0 = nt * OT_N;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 64;
   const uint16_t* Ag = A + grp * a_goff;
   const uint16_t* Wg = W + grp * w_gstride;
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  for (int k0 = 0; k0 < K; k0 += OT_K) {
-    // 128 rows x 32 k of each operand: 512 chunks of 8 bf16, two per thread
+  // per K-step: A 256 x 32 = 1024 chunks of 8 (4 per thread), W 128 x 32 = 512 (2 per thread)
+  u32x4 ra[4], rw[2];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int idx = tid + 256 * p, r = idx >> 2, kc = (idx & 3) * 8;
+      ra[p] = m0 + r < M ? *reinterpret_cast<const u32x4*>(Ag + (int64_t)(m0 + r) * lda + k0 + kc)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int idx = tid + 256 * p, r = idx >> 2, kc = (idx & 3) * 8;
+      rw[p] = n0 + r < N ? *reinterpret_cast<const u32x4*>(Wg + (int64_t)(n0 + r) * K + k0 + kc)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int idx = tid + 256 * p;
+      *reinterpret_cast<u32x4*>(&As[b][idx >> 2][(idx & 3) * 8]) = ra[p];
+    }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int idx = tid + 256 * p;
-      const int r = idx >> 2, kc = (idx & 3) * 8;
-      u32x4 va = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-      if (m0 + r < M) va = *reinterpret_cast<const u32x4*>(Ag + (int64_t)(m0 + r) * lda + k0 + kc);
-      if (n0 + r < N) vw = *reinterpret_cast<const u32x4*>(Wg + (int64_t)(n0 + r) * K + k0 + kc);
-      *reinterpret_cast<u32x4*>(&As[r][kc]) = va;
-      *reinterpret_cast<u32x4*>(&Ws[r][kc]) = vw;
+      *reinterpret_cast<u32x4*>(&Ws[b][idx >> 2][(idx & 3) * 8]) = rw[p];
     }
-    __syncthreads();
+  };
+  const int nk = K / OT_K;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * OT_K);
 #pragma unroll
     for (int ks = 0; ks < OT_K / 16; ++ks) {
       const int kof = 16 * ks + 8 * (lane >> 5);
-      bf16x8 af[2], wf[2];
+      bf16x8 af[4], wf[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&As[wm + 32 * i + (lane & 31)][kof]));
+      for (int i = 0; i < 4; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&As[cur][wm + 32 * i + (lane & 31)][kof]));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        wf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&Ws[wn + 32 * j + (lane & 31)][kof]));
+        wf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&Ws[cur][wn + 32 * j + (lane & 31)][kof]));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
     }
+    if (kt + 1 < nk) store(cur ^ 1);
     __syncthreads();
   }
   // D: lane holds column l%32, rows 8(r/4) + 4(l/32) + r%4 of each 32 x 32 tile
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int gn = n0 + wn + 32 * j + (lane & 31);
@@ -253,7 +289,8 @@ static hipError_t launch_oproj_gemm(const void* A, int64_t lda, int64_t a_goff, 
     hipLaunchKernelGGL(oproj_reduce_kernel, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0,
                        s, (const float*)part, p_split, splits, C, c_bf16, count);
   } else {
-    dim3 grid((N + OT_N - 1) / OT_N, (M + OT_M - 1) / OT_M, groups);
+    const int64_t nN = (N + OT_N - 1) / OT_N, nM = (M + OT_M - 1) / OT_M;
+    dim3 grid((unsigned)((nM + 7) / 8 * 8 * nN * groups));
     hipLaunchKernelGGL(oproj_tiled_kernel, grid, dim3(256), 0, s, (const uint16_t*)A, lda, a_goff,
                        (const uint16_t*)W, w_gstride, C, ldc, (int64_t)N, c_bf16, M, N, K);
   }
