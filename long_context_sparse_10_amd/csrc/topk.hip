@@ -11,7 +11,9 @@
 // registers: thread t owns the contiguous entries [16 t, 16 t + 16).  The
 // first digit is counted block-wide; the keys sharing it with the k-th largest
 // (the candidates) are compacted into LDS and one wave resolves the remaining
-// digits over them alone; the ordered compaction is a single block-wide scan.  Longer rows (few decode rows over 2^18 entries) spread over
+// digits over them alone (past TK_CAND_CAP candidates the block resolves them
+// over the keys in registers instead); the ordered compaction is a single
+// block-wide scan.  Longer rows (few decode rows over 2^18 entries) spread over
 // many blocks per row: per-block digit histograms, a per-row reduction that
 // fixes the digit, and after the last digit per-block counts and an ordered
 // emit at each block's offset.
@@ -162,19 +164,24 @@ __device__ __forceinline__ int wave_scan_excl(int v, int* total) {
   return x - v;
 }
 
+// candidates compacted for the last digits (more go the block-wide way): a
+// small buffer keeps more rows resident per CU when many short rows run
+constexpr int TK_CAND_CAP = 2048;
+
 template <bool BF16>
 __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ scores,
                                                     const int32_t* __restrict__ q_pos,
                                                     const int32_t* __restrict__ n_entries, int Tq,
                                                     int Nmax, int m, int k, int vec,
                                                     int32_t* __restrict__ idx) {
-  __shared__ int hist[8192];
-  extern __shared__ uint32_t cand[];  // [16 * blockDim]: keys sharing the k-th's first digit
+  __shared__ int hist[BF16 ? 1024 : 8192];
+  extern __shared__ uint32_t cand[];  // [min(16 * blockDim, TK_CAND_CAP)]: keys sharing the k-th's first digit
   __shared__ int scan_ws[16];
   __shared__ uint32_t sh_digit;
   __shared__ int sh_above, sh_ncand;
   const int row = blockIdx.x, b = row / Tq;
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
+  const int cap = min(16 * nt, TK_CAND_CAP);
   const int nv = min(min(n_entries[b], Nmax), (q_pos[row] + 1) / m);
   int32_t* out = idx + (int64_t)row * k;
   const void* srow = BF16 ? (const void*)((const uint16_t*)scores + (int64_t)row * Nmax)
@@ -219,13 +226,44 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
     pos += __shfl(base, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (s0 + i < nv && (key[i] >> SH1) == d1) cand[pos++] = key[i];
+      if (s0 + i < nv && (key[i] >> SH1) == d1) {
+        if (pos < cap) cand[pos] = key[i];
+        ++pos;
+      }
   }
   __syncthreads();
-  // ---- remaining digits over the candidates by wave 0 alone (no block barriers):
-  // fp32 keys 10 + 9 bits (18..9, 8..0), bf16 keys 6 bits (5..0)
-  if (tid < 64) {
-    const int nc = sh_ncand;
+  const int nc = sh_ncand;
+  if (nc > cap) {
+    // ---- too many candidates to compact: the remaining digits block-wide over
+    // the keys in registers (same digits, same rule)
+    uint32_t prefix = d1 << SH1, pmask = ~0u << SH1;
+    int shift = SH1;
+    while (shift > 0) {
+      const int width = BF16 ? 6 : (shift == 19 ? 10 : 9);
+      shift -= width;
+      const int nbins = 1 << width;
+      const uint32_t dmask = (uint32_t)nbins - 1u;
+      for (int i = tid; i < nbins; i += nt) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (s0 + i < nv && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dmask], 1);
+      __syncthreads();
+      find_digit(hist, nbins, remaining, &sh_digit, &sh_above);
+      __syncthreads();
+      const uint32_t dg = sh_digit;
+      remaining -= sh_above;
+      prefix |= dg << shift;
+      pmask |= dmask << shift;
+      __syncthreads();  // every thread has read this digit
+    }
+    if (tid == 0) {
+      sh_digit = prefix;
+      sh_above = remaining;
+    }
+  } else if (tid < 64) {
+    // ---- remaining digits over the candidates by wave 0 alone (no block barriers):
+    // fp32 keys 10 + 9 bits (18..9, 8..0), bf16 keys 6 bits (5..0)
     uint32_t prefix = d1 << SH1, pmask = ~0u << SH1;
     int shift = SH1;
     while (shift > 0) {
@@ -539,7 +577,7 @@ hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_p
   // one block per row, 16 keys per thread (counts stay below 2^16 for the packed scan)
   int threads = 64;  // the smallest power of two >= Nmax / 16, at least one wave
   while (threads * 16 < Nmax) threads *= 2;
-  const size_t cand_bytes = (size_t)16 * threads * sizeof(uint32_t);
+  const size_t cand_bytes = (size_t)(16 * threads < TK_CAND_CAP ? 16 * threads : TK_CAND_CAP) * sizeof(uint32_t);
   if (bf)
     hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(threads), cand_bytes, s, scores,
                        q_pos, n_entries, Tq, Nmax, m, k, vec, idx);

@@ -281,14 +281,16 @@ def test_indexer_generic_f32_and_causal_prefill():
 def _score_rows(rng, kind, rows, N):
     if kind == "ties":
         return rng.integers(-4, 5, size=(rows, N)).astype(np.float32)
-    if kind == "ties81":  # a few hundred tied candidates per row: ranked by comparison
+    if kind == "ties81":  # a few hundred tied candidates per row
         return rng.integers(-40, 41, size=(rows, N)).astype(np.float32)
+    if kind == "ties5":   # thousands of candidates: past the compaction buffer
+        return rng.integers(-2, 3, size=(rows, N)).astype(np.float32)
     if kind == "bf16":
         return I.cast(rng.standard_normal((rows, N)).astype(np.float32) * 0.5, "bf16")
     return rng.standard_normal((rows, N)).astype(np.float32)
 
 
-@pytest.mark.parametrize("kind", ["ties", "ties81", "bf16", "normal"])
+@pytest.mark.parametrize("kind", ["ties", "ties81", "ties5", "bf16", "normal"])
 @pytest.mark.parametrize("N,k,m", [(16384, 1024, 4), (3000, 1024, 4), (700, 32, 4),
                                    (1025, 1024, 4), (40000, 512, 4), (20001, 100, 4),
                                    (262144, 1024, 4)])
