@@ -27,6 +27,13 @@ __device__ __forceinline__ float load_index_elem(const uint8_t* row, const uint8
   return e2m1_to_f32(code) * exp2i((int)scales[j >> 5] - 127);
 }
 
+// ReLU of a matrix-core result in one v_med3_f32: med3(x, 0, FLT_MAX) = max(x, 0)
+// for finite x, without the NaN-quieting max(x, x) the compiler puts in front of
+// fmaxf on values it cannot prove canonical (it doubled the epilogue's VALU work)
+__device__ __forceinline__ float relu_mfma(float x) {
+  return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f);
+}
+
 __global__ __launch_bounds__(256) void indexer_generic_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale, csa_dtype t,
     const float* __restrict__ w, const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale,
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], fmaxf(acc[mt][q], 0.f), sc);
+        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
       sc += __shfl_xor(sc, 16);
       sc += __shfl_xor(sc, 32);
       const int n = base + 16 * g + col;
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(64 * R) void indexer_rows_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], fmaxf(acc[mt][q], 0.f), sc);
+        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
       sc += __shfl_xor(sc, 16);
       sc += __shfl_xor(sc, 32);
       const int n = n0 + col;
@@ -409,7 +416,7 @@ __global__ __launch_bounds__(64 * R) void indexer_rows_mx_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], fmaxf(acc[mt][q], 0.f), sc);
+        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
       sc += __shfl_xor(sc, 16);
       sc += __shfl_xor(sc, 32);
       const int n = n0 + col;
