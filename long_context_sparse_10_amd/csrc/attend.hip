@@ -410,7 +410,11 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
     {                                                                                        \
       const int4* sp4 = reinterpret_cast<const int4*>(&sm.slot[(T) * AT_TILE + 8 * mw]);     \
       const int4 i0 = sp4[0], i1 = sp4[1];                                                   \
-      const int ids[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};                   \
+      /* every lane read the same ids: scalar copies keep the addresses on the SALU */    \
+      const int ids[8] = {__builtin_amdgcn_readfirstlane(i0.x), __builtin_amdgcn_readfirstlane(i0.y), \
+                          __builtin_amdgcn_readfirstlane(i0.z), __builtin_amdgcn_readfirstlane(i0.w), \
+                          __builtin_amdgcn_readfirstlane(i1.x), __builtin_amdgcn_readfirstlane(i1.y), \
+                          __builtin_amdgcn_readfirstlane(i1.z), __builtin_amdgcn_readfirstlane(i1.w)}; \
       _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
         const int id = ids[i];                                                               \
         OK |= (id != -1 ? 1u : 0u) << i;                                                     \
@@ -426,9 +430,16 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
       STG[i] = *reinterpret_cast<const u32x4*>(src[i] + 16 * ch);                            \
   }
 #define CSA_COMMIT(STG, OK, BUF)                                                             \
+  if ((OK) == 0xFFu) {                                                                       \
+    CSA_COMMIT_ROWS(STG, 0xFFu, BUF)                                                         \
+  } else {                                                                                   \
+    CSA_COMMIT_ROWS(STG, OK, BUF)                                                            \
+  }
+  /* (a full set of rows needs no per-row zeroing) */
+#define CSA_COMMIT_ROWS(STG, OK, BUF)                                                        \
   {                                                                                          \
     _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
-      const bool ok_i = (OK >> i) & 1u;                                                      \
+      const bool ok_i = ((OK) >> i) & 1u;                                                    \
       uint16_t* xr = &sm.X[BUF][xrow(8 * mw + i)][0];                                       \
       if (KVF == CSA_BF16) {                                                                 \
         *reinterpret_cast<u32x4*>(xr + 8 * lane) = ok_i ? STG[i] : u32x4{0u, 0u, 0u, 0u};   \
@@ -586,6 +597,7 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
 #undef CSA_TILE
 #undef CSA_STAGE
 #undef CSA_COMMIT
+#undef CSA_COMMIT_ROWS
 #undef CSA_QPREP
 
   // ---- lane holds O^T[dim 16nd + 4g + r][head]; head totals across the 4 groups
