@@ -271,6 +271,13 @@ __device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
       (__attribute__((address_space(3))) s16x4*)(p));
   return __builtin_bit_cast(uint2, v);
 }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// the same read as two lanes of an operand vector (fills half of a quad in place)
+__device__ __forceinline__ u32x2 tr_read2(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 // One block = one query row x 64 heads x one slot split, 8 waves:
 //  * waves 0-3 (math): wave w owns heads 16w..16w+15 and per 32-slot tile runs
@@ -527,18 +534,18 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
         /* O^T += X^T P^T, operands by transpose reads, 8 column blocks ahead */            \
         const uint16_t* c0 = &sm.X[BUF][tr_r0][tr_c];                                        \
         const uint16_t* c1 = &sm.X[BUF][tr_r1][tr_c];                                        \
-        uint2 rx[8][2];                                                                      \
+        /* each pair of 8-byte reads fills the two halves of one operand quad */            \
+        u32x4 rq[8];                                                                         \
         _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                      \
-          rx[q][0] = tr_read(c0 + 16 * q);                                                   \
-          rx[q][1] = tr_read(c1 + 16 * q);                                                   \
+          rq[q].xy = tr_read2(c0 + 16 * q);                                                   \
+          rq[q].zw = tr_read2(c1 + 16 * q);                                                   \
         }                                                                                    \
         _Pragma("unroll") for (int nd = 0; nd < 32; ++nd) {                                  \
-          const u32x4 xa = u32x4{rx[nd & 7][0].x, rx[nd & 7][0].y, rx[nd & 7][1].x, rx[nd & 7][1].y}; \
+          O[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rq[nd & 7]), pf, O[nd], 0, 0, 0); \
           if (nd + 8 < 32) {                                                                 \
-            rx[nd & 7][0] = tr_read(c0 + 16 * (nd + 8));                                     \
-            rx[nd & 7][1] = tr_read(c1 + 16 * (nd + 8));                                     \
+            rq[nd & 7].xy = tr_read2(c0 + 16 * (nd + 8));                                     \
+            rq[nd & 7].zw = tr_read2(c1 + 16 * (nd + 8));                                     \
           }                                                                                  \
-          O[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa), pf, O[nd], 0, 0, 0); \
         }                                                                                    \
         __builtin_amdgcn_sched_group_barrier(0x100, 16, 2);                                  \
         _Pragma("unroll") for (int nd = 0; nd < 24; ++nd) {                                  \
