@@ -40,26 +40,26 @@ METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP
 # of known size (--copy-probe).  An entry holds for the kernel source it was
 # taken on (sha256 of the .hip file); after any change it reports null.
 TRAFFIC = {
-    "decode_64k": dict(src="indexer.hip", sha256="213e05c5c94a7cbb737f73159c9137fecde78845a8e2d6980bc8c315f6a8e8ac",
-                fetch_kib=67679.0, write_kib=2048.9, fetch_scale=1.9998,
+    "decode_64k": dict(src="indexer.hip", sha256="b66562989b06ce07e808673a2482c3da4cb9f380f4136657f0f3460d2d780dfc",
+                fetch_kib=67679.0, write_kib=2048.7, fetch_scale=1.9998,
                 write_scale=1.0),
-    "hca_decode_1m": dict(src="attend.hip", sha256="ee655a444067cb9d95284cd40f59c81b3355a772a183c3e8df29436863cccf48",
-                fetch_kib=76325.6, write_kib=18560.0, fetch_scale=1.9998,
+    "hca_decode_1m": dict(src="attend.hip", sha256="79509f3f90e2cfeeeca7b7ea2837c98a6cf270d73033536a1f08942abaea2899",
+                fetch_kib=75783.5, write_kib=17536.0, fetch_scale=1.9998,
                 write_scale=1.0),
-    "decode_1m_fp4": dict(src="indexer.hip", sha256="213e05c5c94a7cbb737f73159c9137fecde78845a8e2d6980bc8c315f6a8e8ac",
-                fetch_kib=69948.9, write_kib=4096.1, fetch_scale=1.9998,
+    "decode_1m_fp4": dict(src="indexer.hip", sha256="b66562989b06ce07e808673a2482c3da4cb9f380f4136657f0f3460d2d780dfc",
+                fetch_kib=69948.8, write_kib=4096.1, fetch_scale=1.9998,
                 write_scale=1.0),
-    "prefill_32k": dict(src="attend.hip", sha256="ee655a444067cb9d95284cd40f59c81b3355a772a183c3e8df29436863cccf48",
-                fetch_kib=3361022.1, write_kib=2222125.1, fetch_scale=1.9998,
+    "prefill_32k": dict(src="attend.hip", sha256="79509f3f90e2cfeeeca7b7ea2837c98a6cf270d73033536a1f08942abaea2899",
+                fetch_kib=3294813.5, write_kib=2097203.4, fetch_scale=1.9998,
                 write_scale=1.0),
-    "prefill_32k_mxfp4": dict(src="attend.hip", sha256="ee655a444067cb9d95284cd40f59c81b3355a772a183c3e8df29436863cccf48",
-                fetch_kib=3364576.3, write_kib=2223454.5, fetch_scale=1.9998,
+    "prefill_32k_mxfp4": dict(src="attend.hip", sha256="79509f3f90e2cfeeeca7b7ea2837c98a6cf270d73033536a1f08942abaea2899",
+                fetch_kib=3304052.0, write_kib=2097216.0, fetch_scale=1.9998,
                 write_scale=1.0),
-    "oproj_decode": dict(src="oproj.hip", sha256="06319b9ca96d03bb318e747f4f43e1700e84cf3614483fca35e959f5e807318e",
-                fetch_kib=80952.1, write_kib=8969.2, fetch_scale=1.9998,
+    "oproj_decode": dict(src="oproj.hip", sha256="233800c0b523f5652c1ca82c87ce43f04b49013854953988b76bc4eeb6b99009",
+                fetch_kib=80947.3, write_kib=8970.1, fetch_scale=1.9998,
                 write_scale=1.0),
-    "oproj_prefill": dict(src="oproj.hip", sha256="06319b9ca96d03bb318e747f4f43e1700e84cf3614483fca35e959f5e807318e",
-                fetch_kib=12924029.9, write_kib=952182.6, fetch_scale=1.9998,
+    "oproj_prefill": dict(src="oproj.hip", sha256="233800c0b523f5652c1ca82c87ce43f04b49013854953988b76bc4eeb6b99009",
+                fetch_kib=6491159.2, write_kib=806256.8, fetch_scale=1.9998,
                 write_scale=1.0),
 }
 
