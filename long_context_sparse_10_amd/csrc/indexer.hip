@@ -88,7 +88,8 @@ __device__ __forceinline__ i32x8 widen(u32x4 v) {
 //  * MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4, one instruction per tile: lane
 //    kg holds code bytes 16kg .. 16kg+15 (dims 32kg .. 32kg+31), exactly the
 //    32-element block whose e8m0 scale the matrix core applies.
-// A wave scores G groups of 16 entries per step (bf16 G = 2, MXFP4 G = 8) and
+// A wave scores G groups of 16 entries per step (bf16 G = 2, MXFP4 G = 8),
+// reduces the head sum of two groups at a time across its four lane rows, and
 // keeps a ring of three steps of raw key bytes in registers: two in flight
 // while the third is scored.
 template <bool MX>
@@ -173,34 +174,49 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
   };
   auto process = [&](const Raw& r, int base) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      f32x4 acc[4];
+    for (int gp = 0; gp < G; gp += 2) {
+      float part[2];  // this lane's share (heads 16mt + 4kg + r) of groups gp, gp + 1
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (!MX) {
+      for (int h = 0; h < 2; ++h) {
+        const int g = gp + h;
+        f32x4 acc[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 bk = __builtin_bit_cast(bf16x8, r.v[4 * g + ks]);
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!MX) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 bk = __builtin_bit_cast(bf16x8, r.v[4 * g + ks]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][MX ? 0 : ks], bk, acc[mt], 0, 0, 0);
+          }
+        } else {
+          const i32x8 bk = widen(r.v[g]);
+          const int bs = (int)(r.sc[MX ? g : 0] >> (8 * kg));
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][MX ? 0 : ks], bk, acc[mt], 0, 0, 0);
+            acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(aq[mt]), bk, acc[mt], 4, 4, 0, asc[mt], 0, bs);
         }
-      } else {
-        const i32x8 bk = widen(r.v[g]);
-        const int bs = (int)(r.sc[MX ? g : 0] >> (8 * kg));
+        float sc = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(aq[mt]), bk, acc[mt], 4, 4, 0, asc[mt], 0, bs);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
+        part[h] = sc;
       }
-      float sc = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
-      sc += __shfl_xor(sc, 16);
-      sc += __shfl_xor(sc, 32);
-      const int n = base + 16 * g + col;
-      if (kg == 0 && n < e1) {
+      // Sum the four 16-lane rows (kg) of both groups with two lane swaps on
+      // the VALU.  The 16-lane swap exchanges odd rows of the first operand
+      // with even rows of the second: rows become (g0: kg 0+1, g1: kg 0+1,
+      // g0: kg 2+3, g1: kg 2+3); the 32-lane swap then adds the upper half to
+      // the lower, so lane l < 32 ends with the score of entry 16 gp + l.
+      const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[0]),
+                                                     __float_as_uint(part[1]), false, false);
+      const float t = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+      const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
+                                                     false, false);
+      const float sc = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      const int n = base + 16 * gp + lane;
+      if (lane < 32 && n < e1) {
         const int64_t o = (int64_t)row * Nmax + n;
         if (score_bf16)
           reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(sc);
