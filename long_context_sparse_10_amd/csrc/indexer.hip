@@ -101,38 +101,16 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
     void* __restrict__ scores, int score_bf16, PageMap pg) {
   constexpr int G = MX ? 8 : 2;
   constexpr int64_t RB = MX ? 64 : 256;  // key row bytes
+  extern __shared__ __attribute__((aligned(16))) uint32_t sbuf[];  // the block's scores
   const int tiles = (Nmax + ent_per_block - 1) / ent_per_block;
   const int row = blockIdx.x / tiles, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = lane >> 4, col = lane & 15;
-  const int nv = min(min(n_entries[b], Nmax), (q_pos[row] + 1) / m);
   const int e0 = (blockIdx.x % tiles) * ent_per_block;
-  if (e0 >= nv) return;
-  const int e1 = min(e0 + ent_per_block, nv);
-
-  // query fragments of head 16*mt + col in the keys' K order
-  bf16x8 afr[4][MX ? 1 : 4];
-  u32x4 aq[4];
-  int asc[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int64_t qr = (int64_t)row * 64 + 16 * mt + col;
-    if (!MX) {
-#pragma unroll
-      for (int ks = 0; ks < (MX ? 1 : 4); ++ks)
-        afr[mt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qI + qr * 256 + 64 * ks + 16 * kg));
-    } else {
-      aq[mt] = *reinterpret_cast<const u32x4*>(qI + qr * 64 + 16 * kg);
-      asc[mt] = (int)(*reinterpret_cast<const uint32_t*>(qI_scale + qr * 4) >> (8 * kg));
-    }
-  }
-  // weights of the head rows this lane's accumulators hold: register r of
-  // tile mt is head 16*mt + 4*kg + r
-  float wr[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wr[mt][r] = w[(int64_t)row * 64 + 16 * mt + 4 * kg + r];
+  // dense rows: the first two steps are fetched before the visible-entry
+  // count arrives (rows up to the block's end or Nmax are in bounds; scores
+  // past the count are not written).  Paged rows wait for the count.
+  int e1 = min(e0 + ent_per_block, Nmax);
 
   struct Raw {
     u32x4 v[MX ? G : 4 * G];
@@ -172,6 +150,45 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
       }
     }
   };
+  constexpr int STEP = IDX_WAVES * 16 * G;
+  int base = e0 + wave * 16 * G;
+  Raw r0, r1, r2;
+  if (!pg.paged()) {
+    if (base < e1) fetch(base, r0);
+    if (base + STEP < e1) fetch(base + STEP, r1);
+  }
+  const int nv = min(min(n_entries[b], Nmax), (q_pos[row] + 1) / m);
+  if (e0 >= nv) return;
+  e1 = min(e1, nv);
+  if (pg.paged()) {
+    if (base < e1) fetch(base, r0);
+    if (base + STEP < e1) fetch(base + STEP, r1);
+  }
+
+  // query fragments of head 16*mt + col in the keys' K order
+  bf16x8 afr[4][MX ? 1 : 4];
+  u32x4 aq[4];
+  int asc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t qr = (int64_t)row * 64 + 16 * mt + col;
+    if (!MX) {
+#pragma unroll
+      for (int ks = 0; ks < (MX ? 1 : 4); ++ks)
+        afr[mt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qI + qr * 256 + 64 * ks + 16 * kg));
+    } else {
+      aq[mt] = *reinterpret_cast<const u32x4*>(qI + qr * 64 + 16 * kg);
+      asc[mt] = (int)(*reinterpret_cast<const uint32_t*>(qI_scale + qr * 4) >> (8 * kg));
+    }
+  }
+  // weights of the head rows this lane's accumulators hold: register r of
+  // tile mt is head 16*mt + 4*kg + r
+  float wr[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wr[mt][r] = w[(int64_t)row * 64 + 16 * mt + 4 * kg + r];
+
   auto process = [&](const Raw& r, int base) {
 #pragma unroll
     for (int gp = 0; gp < G; gp += 2) {
@@ -217,19 +234,13 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
       const float sc = __uint_as_float(y[0]) + __uint_as_float(y[1]);
       const int n = base + 16 * gp + lane;
       if (lane < 32 && n < e1) {
-        const int64_t o = (int64_t)row * Nmax + n;
         if (score_bf16)
-          reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(sc);
+          reinterpret_cast<uint16_t*>(sbuf)[n - e0] = (uint16_t)f32_to_bf16(sc);
         else
-          reinterpret_cast<float*>(scores)[o] = sc;
+          sbuf[n - e0] = __float_as_uint(sc);
       }
     }
   };
-  constexpr int STEP = IDX_WAVES * 16 * G;
-  int base = e0 + wave * 16 * G;
-  Raw r0, r1, r2;
-  if (base < e1) fetch(base, r0);
-  if (base + STEP < e1) fetch(base + STEP, r1);
   for (; base < e1; base += 3 * STEP) {
     if (base + 2 * STEP < e1) fetch(base + 2 * STEP, r2);
     process(r0, base);
@@ -239,6 +250,22 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
     if (base + 2 * STEP >= e1) break;
     if (base + 4 * STEP < e1) fetch(base + 4 * STEP, r1);
     process(r2, base + 2 * STEP);
+  }
+  // the block's scores leave once, after the key stream: a store issued
+  // between key loads would hold up the in-order wait for the next key step
+  __syncthreads();
+  const int len = e1 - e0;
+  const int64_t o0 = (int64_t)row * Nmax + e0;
+  const int per16 = score_bf16 ? 8 : 4;  // scores per 16 bytes
+  uint8_t* dst = reinterpret_cast<uint8_t*>(scores) + o0 * (score_bf16 ? 2 : 4);
+  const int nvec = ((uintptr_t)dst & 15) == 0 ? len / per16 : 0;
+  for (int i = threadIdx.x; i < nvec; i += IDX_WAVES * 64)
+    reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(sbuf)[i];
+  for (int i = nvec * per16 + threadIdx.x; i < len; i += IDX_WAVES * 64) {
+    if (score_bf16)
+      reinterpret_cast<uint16_t*>(dst)[i] = reinterpret_cast<const uint16_t*>(sbuf)[i];
+    else
+      reinterpret_cast<uint32_t*>(dst)[i] = sbuf[i];
   }
 }
 
@@ -482,12 +509,13 @@ hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_
     int epb = (int)(((want + step - 1) / step) * step);
     epb = epb < 2 * step ? 2 * step : (epb > 8192 ? 8192 : epb);
     dim3 grid((unsigned)(((int64_t)Nmax + epb - 1) / epb * rows));
+    const size_t shm = (size_t)epb * (sbf ? 2 : 4);
     if (in_t == CSA_BF16)
-      hipLaunchKernelGGL(indexer_mfma_kernel<false>, grid, dim3(IDX_WAVES * 64), 0, s,
+      hipLaunchKernelGGL(indexer_mfma_kernel<false>, grid, dim3(IDX_WAVES * 64), shm, s,
                          (const uint8_t*)qI, qI_scale, w, (const uint8_t*)kI, kI_scale, q_pos,
                          n_entries, Tq, Nmax, m, epb, scores, sbf, pg);
     else
-      hipLaunchKernelGGL(indexer_mfma_kernel<true>, grid, dim3(IDX_WAVES * 64), 0, s,
+      hipLaunchKernelGGL(indexer_mfma_kernel<true>, grid, dim3(IDX_WAVES * 64), shm, s,
                          (const uint8_t*)qI, qI_scale, w, (const uint8_t*)kI, kI_scale, q_pos,
                          n_entries, Tq, Nmax, m, epb, scores, sbf, pg);
   } else {
