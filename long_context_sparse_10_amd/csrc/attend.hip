@@ -18,7 +18,11 @@
 //    v_mfma_f32_16x16x32_bf16 with an fp32 online softmax in registers.
 //    With one split the block finishes the output itself; otherwise it writes
 //    per-split (m, l) and O / l (bf16) and attend_combine_kernel merges the
-//    splits in order.
+//    splits in order.  Used for FP8 rows and for split slot lists (decode):
+//    its register ring keeps four tiles in flight per block.
+//  * attend_pf_kernel     -- the same math for bf16 rows when the slot list is
+//    not split (prefill, short lists): 256-thread blocks, two per compute
+//    unit, each wave loading its own rows straight into shared memory.
 //  * attend_generic_kernel -- any shape / fp32: one wave per head, VALU.
 #include "common.hpp"
 #include "internal.hpp"
@@ -279,6 +283,139 @@ __device__ __forceinline__ u32x2 tr_read2(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Final output of one lane's head (single slot split): the sink joins the
+// denominator, the row is normalised, and its RoPE channels are rotated back
+// by -q (rcs holds cos / sin of the query position per RoPE pair).  The lane
+// holds O^T[dim 16nd + 4g + r][head] in log2-unit softmax state (m_run, l_tot).
+__device__ __forceinline__ void attend_store_out(const AttendArgs& a, int row, int head, int g,
+                                                 const f32x4* O, float m_run, float l_tot,
+                                                 const float (*rcs)[2]) {
+  const int d_r = a.rope_dims;
+  const float z = a.sink[head] * kLog2e;  // sink in log2 units
+  const float M = fmaxf(m_run, z);
+  const float em = exp2f_hw(m_run - M);
+  const float f = em / (l_tot * em + exp2f_hw(z - M));
+  uint8_t* orow = (uint8_t*)a.out + ((int64_t)row * a.nh + head) * row_bytes(a.out_t, AT_C, 0);
+#pragma unroll
+  for (int nd = 0; nd < 32; ++nd) {
+    const int d0 = 16 * nd + 4 * g;
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = O[nd][r] * f;
+    if (16 * nd + 16 > AT_C - d_r) {
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        if (d0 + r >= AT_C - d_r) {
+          const float cs = rcs[(d0 + r - (AT_C - d_r)) >> 1][0];
+          const float sn = -rcs[(d0 + r - (AT_C - d_r)) >> 1][1];
+          const float x0 = v[r], x1 = v[r + 1];
+          v[r] = x0 * cs - x1 * sn;
+          v[r + 1] = x0 * sn + x1 * cs;
+        }
+      }
+    }
+    if (a.out_t == CSA_F32) {
+      *reinterpret_cast<f32x4*>(orow + 4 * d0) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+      *reinterpret_cast<uint2*>(orow + 2 * d0) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+  }
+}
+
+// One 32-slot tile on a math wave of 16 heads (reads X[BUF] of the block's
+// shared memory; needs qf, m_run, l_run, O, li, g and the transpose-read
+// addresses tr_r0 / tr_r1 / tr_c in scope): S^T, online softmax, O^T.  RAD
+// and RQD are how many S^T operand quads and P.V operand quads are read ahead.
+#define CSA_TILE(T, BUF, RAD, RQD)                                                            \
+{                                                                                             \
+  const uint32_t mask = sm.vmask[T];                                                          \
+  if (mask != 0u) {                                                                           \
+    f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};                      \
+    {                                                                                         \
+      const uint16_t* xr0 = &sm.X[BUF][xrow(8 * (li >> 2) + (li & 3))][128 * g];              \
+      const uint16_t* xr1 = &sm.X[BUF][xrow(8 * (li >> 2) + 4 + (li & 3))][128 * g];          \
+      u32x4 ra[RAD], rb4[RAD];                                                                \
+      _Pragma("unroll") for (int q = 0; q < (RAD); ++q) {                                     \
+        ra[q] = *reinterpret_cast<const u32x4*>(xr0 + 8 * q);                                 \
+        rb4[q] = *reinterpret_cast<const u32x4*>(xr1 + 8 * q);                                \
+      }                                                                                       \
+      _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                     \
+        const u32x4 a0 = ra[ks % (RAD)], a1 = rb4[ks % (RAD)];                                \
+        if (ks + (RAD) < 16) {                                                                \
+          ra[ks % (RAD)] = *reinterpret_cast<const u32x4*>(xr0 + 8 * (ks + (RAD)));           \
+          rb4[ks % (RAD)] = *reinterpret_cast<const u32x4*>(xr1 + 8 * (ks + (RAD)));          \
+        }                                                                                     \
+        S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qf[ks], S[0], 0, 0, 0); \
+        S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qf[ks], S[1], 0, 0, 0); \
+      }                                                                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (RAD), 1);                              \
+      _Pragma("unroll") for (int ks = 0; ks < 16 - (RAD); ++ks) {                             \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);                                    \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);                                    \
+      }                                                                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * (RAD), 1);                              \
+    }                                                                                         \
+    /* logits in log2 units (the queries carry tau * log2 e); masked slots -inf */            \
+    float lg[8];                                                                              \
+    _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                          \
+    _Pragma("unroll") for (int r = 0; r < 4; ++r) lg[4 * nt + r] = S[nt][r];                  \
+    if (mask != 0xFFFFFFFFu) {                                                                \
+      _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                        \
+      _Pragma("unroll") for (int r = 0; r < 4; ++r)                                           \
+        if (!((mask >> (8 * g + 4 * nt + r)) & 1u)) lg[4 * nt + r] = -INFINITY;               \
+    }                                                                                         \
+    float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),                         \
+                     fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));                        \
+    /* lazy rescale: the reference maximum moves only when a logit exceeds it */              \
+    /* by more than 8 nats (weights stay below e^8: safe in fp32 sums and bf16 P). */         \
+    /* The max across the head's four lane groups is taken only then. */                      \
+    if (__any(mx > m_run + kLazy2)) {                                                         \
+      mx = fmaxf(mx, __shfl_xor(mx, 16));                                                     \
+      mx = fmaxf(mx, __shfl_xor(mx, 32));                                                     \
+      const bool grow = mx > m_run + kLazy2;                                                  \
+      const float m_new = grow ? mx : m_run;                                                  \
+      const float alpha = exp2f_hw(m_run - m_new);                                            \
+      l_run *= alpha;                                                                         \
+      m_run = m_new;                                                                          \
+      _Pragma("unroll") for (int nd = 0; nd < 32; ++nd) O[nd] *= alpha;                       \
+    }                                                                                         \
+    float pv[8], ps = 0.f;                                                                    \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                           \
+      pv[i] = exp2f_hw(lg[i] - m_run);                                                        \
+      ps += pv[i];                                                                            \
+    }                                                                                         \
+    l_run += ps;                                                                              \
+    u32x4 pk;                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2_hw(pv[2 * i], pv[2 * i + 1]); \
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk); /* P^T: entries 8g..8g+7 of head li */  \
+    {                                                                                         \
+      /* O^T += X^T P^T, operands by transpose reads, 8 column blocks ahead */                \
+      const uint16_t* c0 = &sm.X[BUF][tr_r0][tr_c];                                           \
+      const uint16_t* c1 = &sm.X[BUF][tr_r1][tr_c];                                           \
+      /* each pair of 8-byte reads fills the two halves of one operand quad */                \
+      u32x4 rq[RQD];                                                                          \
+      _Pragma("unroll") for (int q = 0; q < (RQD); ++q) {                                     \
+        rq[q].xy = tr_read2(c0 + 16 * q);                                                     \
+        rq[q].zw = tr_read2(c1 + 16 * q);                                                     \
+      }                                                                                       \
+      _Pragma("unroll") for (int nd = 0; nd < 32; ++nd) {                                     \
+        O[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rq[nd % (RQD)]), pf, O[nd], 0, 0, 0); \
+        if (nd + (RQD) < 32) {                                                                \
+          rq[nd % (RQD)].xy = tr_read2(c0 + 16 * (nd + (RQD)));                               \
+          rq[nd % (RQD)].zw = tr_read2(c1 + 16 * (nd + (RQD)));                               \
+        }                                                                                     \
+      }                                                                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (RQD), 2);                              \
+      _Pragma("unroll") for (int nd = 0; nd < 32 - (RQD); ++nd) {                             \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                    \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);                                    \
+      }                                                                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, RQD, 2);                                    \
+    }                                                                                         \
+  }                                                                                           \
+}
+
 // One block = one query row x 64 heads x one slot split, 8 waves:
 //  * waves 0-3 (math): wave w owns heads 16w..16w+15 and per 32-slot tile runs
 //      S^T[e][h] = X[e] . q_h       v_mfma_f32_16x16x32_bf16, A = rows, B = q (LDS)
@@ -467,95 +604,6 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   const int tr_r0 = xrow(8 * g + (li >> 2)), tr_r1 = xrow(8 * g + 4 + (li >> 2));
   const int tr_c = 4 * (li & 3);
 
-  // one tile on the math waves: S^T, online softmax, O^T (reads X[BUF])
-#define CSA_TILE(T, BUF)                                                                     \
-  {                                                                                          \
-    const uint32_t mask = sm.vmask[T];                                                       \
-    if (mask != 0u) {                                                                        \
-      f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};                    \
-      {                                                                                      \
-        const uint16_t* xr0 = &sm.X[BUF][xrow(8 * (li >> 2) + (li & 3))][128 * g];          \
-        const uint16_t* xr1 = &sm.X[BUF][xrow(8 * (li >> 2) + 4 + (li & 3))][128 * g];      \
-        u32x4 ra[3], rb4[3];                                                                 \
-        _Pragma("unroll") for (int q = 0; q < 3; ++q) {                                      \
-          ra[q] = *reinterpret_cast<const u32x4*>(xr0 + 8 * q);                              \
-          rb4[q] = *reinterpret_cast<const u32x4*>(xr1 + 8 * q);                             \
-        }                                                                                    \
-        _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                  \
-          const u32x4 a0 = ra[ks % 3], a1 = rb4[ks % 3];                                     \
-          if (ks + 3 < 16) {                                                                 \
-            ra[ks % 3] = *reinterpret_cast<const u32x4*>(xr0 + 8 * (ks + 3));                \
-            rb4[ks % 3] = *reinterpret_cast<const u32x4*>(xr1 + 8 * (ks + 3));               \
-          }                                                                                  \
-          S[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qf[ks], S[0], 0, 0, 0); \
-          S[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qf[ks], S[1], 0, 0, 0); \
-        }                                                                                    \
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);                                   \
-        _Pragma("unroll") for (int ks = 0; ks < 13; ++ks) {                                  \
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);                                 \
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);                                 \
-        }                                                                                    \
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);                                   \
-      }                                                                                      \
-      /* logits in log2 units (the queries carry tau * log2 e); masked slots -inf */       \
-      float lg[8];                                                                           \
-      _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                       \
-      _Pragma("unroll") for (int r = 0; r < 4; ++r) lg[4 * nt + r] = S[nt][r];               \
-      if (mask != 0xFFFFFFFFu) {                                                             \
-        _Pragma("unroll") for (int nt = 0; nt < 2; ++nt)                                     \
-        _Pragma("unroll") for (int r = 0; r < 4; ++r)                                        \
-          if (!((mask >> (8 * g + 4 * nt + r)) & 1u)) lg[4 * nt + r] = -INFINITY;            \
-      }                                                                                      \
-      float mx = fmaxf(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])),                      \
-                       fmaxf(fmaxf(lg[4], lg[5]), fmaxf(lg[6], lg[7])));                     \
-      /* lazy rescale: the reference maximum moves only when a logit exceeds it */          \
-      /* by more than 8 nats (weights stay below e^8: safe in fp32 sums and bf16 P). */     \
-      /* The max across the head's four lane groups is taken only then. */                  \
-      if (__any(mx > m_run + kLazy2)) {                                                      \
-        mx = fmaxf(mx, __shfl_xor(mx, 16));                                                  \
-        mx = fmaxf(mx, __shfl_xor(mx, 32));                                                  \
-        const bool grow = mx > m_run + kLazy2;                                               \
-        const float m_new = grow ? mx : m_run;                                               \
-        const float alpha = exp2f_hw(m_run - m_new);                                         \
-        l_run *= alpha;                                                                      \
-        m_run = m_new;                                                                       \
-        _Pragma("unroll") for (int nd = 0; nd < 32; ++nd) O[nd] *= alpha;                    \
-      }                                                                                      \
-      float pv[8], ps = 0.f;                                                                 \
-      _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                        \
-        pv[i] = exp2f_hw(lg[i] - m_run);                                                     \
-        ps += pv[i];                                                                         \
-      }                                                                                      \
-      l_run += ps;                                                                           \
-      u32x4 pk;                                                                              \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2_hw(pv[2 * i], pv[2 * i + 1]); \
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pk); /* P^T: entries 8g..8g+7 of head li */ \
-      {                                                                                      \
-        /* O^T += X^T P^T, operands by transpose reads, 8 column blocks ahead */            \
-        const uint16_t* c0 = &sm.X[BUF][tr_r0][tr_c];                                        \
-        const uint16_t* c1 = &sm.X[BUF][tr_r1][tr_c];                                        \
-        /* each pair of 8-byte reads fills the two halves of one operand quad */            \
-        u32x4 rq[8];                                                                         \
-        _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                      \
-          rq[q].xy = tr_read2(c0 + 16 * q);                                                   \
-          rq[q].zw = tr_read2(c1 + 16 * q);                                                   \
-        }                                                                                    \
-        _Pragma("unroll") for (int nd = 0; nd < 32; ++nd) {                                  \
-          O[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rq[nd & 7]), pf, O[nd], 0, 0, 0); \
-          if (nd + 8 < 32) {                                                                 \
-            rq[nd & 7].xy = tr_read2(c0 + 16 * (nd + 8));                                     \
-            rq[nd & 7].zw = tr_read2(c1 + 16 * (nd + 8));                                     \
-          }                                                                                  \
-        }                                                                                    \
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 2);                                  \
-        _Pragma("unroll") for (int nd = 0; nd < 24; ++nd) {                                  \
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);                                 \
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);                                 \
-        }                                                                                    \
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 2);                                   \
-      }                                                                                      \
-    }                                                                                        \
-  }
 
   if (!math) {
     // ---- loaders: a ring of 2 register sets; tile u lives in set u % 2.
@@ -598,10 +646,9 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   for (int ks = 0; ks < 16; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8*>(&sm.Q[16 * mw + li][128 * g + 8 * ks]);
   for (int t = 0; t < ntiles; ++t) {
-    CSA_TILE(t, t & 1);
+    CSA_TILE(t, t & 1, 3, 8);
     __syncthreads();
   }
-#undef CSA_TILE
 #undef CSA_STAGE
 #undef CSA_COMMIT
 #undef CSA_COMMIT_ROWS
@@ -612,36 +659,7 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (nsplit == 1) {
-    const float z = a.sink[head] * kLog2e;  // sink in log2 units
-    const float M = fmaxf(m_run, z);
-    const float em = exp2f_hw(m_run - M);
-    const float f = em / (l_tot * em + exp2f_hw(z - M));
-    uint8_t* orow = (uint8_t*)a.out + ((int64_t)row * a.nh + head) * row_bytes(a.out_t, AT_C, 0);
-#pragma unroll
-    for (int nd = 0; nd < 32; ++nd) {
-      const int d0 = 16 * nd + 4 * g;
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = O[nd][r] * f;
-      if (16 * nd + 16 > AT_C - d_r) {
-#pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-          if (d0 + r >= AT_C - d_r) {
-            const float cs = sm.rcs[(d0 + r - (AT_C - d_r)) >> 1][0];
-            const float sn = -sm.rcs[(d0 + r - (AT_C - d_r)) >> 1][1];
-            const float x0 = v[r], x1 = v[r + 1];
-            v[r] = x0 * cs - x1 * sn;
-            v[r + 1] = x0 * sn + x1 * cs;
-          }
-        }
-      }
-      if (a.out_t == CSA_F32) {
-        *reinterpret_cast<f32x4*>(orow + 4 * d0) = f32x4{v[0], v[1], v[2], v[3]};
-      } else {
-        *reinterpret_cast<uint2*>(orow + 2 * d0) =
-            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
-    }
+    attend_store_out(a, row, head, g, O, m_run, l_tot, sm.rcs);
   } else {
     // partials: O / l in bf16 [rows, nsplit, nh, 512], then (m, l) fp32
     // [rows, nsplit, nh, 2].  Each split's O / l is a convex combination of
@@ -662,6 +680,185 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
     }
   }
 }
+
+// ============================================================ MFMA, two blocks per CU
+// Many query rows over bf16 rows (prefill, and short lists): one 256-thread
+// block per (query row, 64 heads) over the whole slot list, two blocks
+// resident per compute unit.  Each of the 4 waves owns 16 heads and also
+// gathers 8 rows of every tile, straight into shared memory (global_load_lds,
+// 16 bytes per lane, one tile ahead of the math).  With two blocks per CU,
+// every SIMD runs two math waves of different query rows, so one wave's
+// softmax, loads and barrier waits overlap the other's matrix-core work; the
+// single-block kernel above has one math wave per SIMD beside a loader.
+// Queries are normalised and rotated in registers (no shared copy), and empty
+// slots are not loaded: their tile rows hold zeros or an earlier valid row,
+// and their weights are 0.
+constexpr int PF_ROPE_MAX = 64;  // RoPE dims (the rotation table is sized for these)
+
+struct AttendPfSmem {
+  uint16_t X[2][AT_TILE][AT_LDX];  // gathered rows (double-buffered tiles), rows permuted by xrow
+  int32_t slot[AT_TAB + 64];
+  uint32_t vmask[AT_TAB / 32 + 2];
+  float rcs[PF_ROPE_MAX / 2][2];   // cos / sin of the query position for each RoPE pair
+};
+
+__global__ __launch_bounds__(256, 2) void attend_pf_kernel(AttendArgs a, Rope rt, int per_xcd) {
+  __shared__ __attribute__((aligned(16))) AttendPfSmem sm;
+  const int hgroups = a.nh / 64;
+  // XCD x (blocks i with i % 8 == x) takes a contiguous run of (row, head
+  // group) pairs: neighbouring query rows select overlapping rows, which are
+  // then fetched into one L2
+  const int lin = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (lin >= a.B * a.Tq * hgroups) return;
+  const int row = lin / hgroups, hg = lin % hgroups;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int head = 64 * hg + 16 * w + li;  // the head of this lane's softmax state
+  const int d_r = a.rope_dims;
+  const float qscale = a.scale * kLog2e;  // queries carry tau * log2 e: logits in log2 units
+  const SlotCtx ctx = make_ctx(a, row);
+  const int total = ctx.kslots + a.n_win;
+  const int ntiles = (total + AT_TILE - 1) / AT_TILE;
+  const int64_t rb = ctx.rb;
+
+  // ---- raw query dims 128g .. 128g+127 of this lane's head, issued first
+  const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)row * a.nh + head) * row_bytes(a.q_t, AT_C, 0);
+  u32x4 qraw[16];
+  if (a.q_t == CSA_BF16) {
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 2 * (128 * g + 8 * ks));
+  }
+  // ---- slot table and per-tile validity masks, RoPE angles, zeroed tiles
+  for (int i = tid; i < ((ntiles * AT_TILE + 63) & ~63); i += 256) {
+    const int id = (i < total) ? slot_row_id(ctx, i) : -1;
+    sm.slot[i] = id;
+    const uint64_t bal = __ballot(id != -1);
+    if (lane == 0) {
+      sm.vmask[i >> 5] = (uint32_t)bal;
+      sm.vmask[(i >> 5) + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  for (int u = tid; u < d_r / 2; u += 256) {
+    float cs, sn;
+    rope_cs(rt, (double)ctx.qp, u, &cs, &sn);
+    sm.rcs[u][0] = cs;
+    sm.rcs[u][1] = sn;
+  }
+  for (int i = tid; i < 2 * AT_TILE * AT_LDX / 8; i += 256)
+    reinterpret_cast<u32x4*>(&sm.X[0][0][0])[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();  // table, angles and zeroed tiles ready
+
+  // ---- gather rows 8w .. 8w+7 of tile T into X[BUF]: one 1 KB row per wave
+  // instruction, lane l bytes 16l .. 16l+15; slot ids are wave-uniform scalars
+#define CSA_PF_LOAD(T, BUF)                                                                  \
+  {                                                                                          \
+    const int4* sp4 = reinterpret_cast<const int4*>(&sm.slot[(T) * AT_TILE + 8 * w]);        \
+    const int4 i0 = sp4[0], i1 = sp4[1];                                                     \
+    const int ids[8] = {__builtin_amdgcn_readfirstlane(i0.x), __builtin_amdgcn_readfirstlane(i0.y), \
+                        __builtin_amdgcn_readfirstlane(i0.z), __builtin_amdgcn_readfirstlane(i0.w), \
+                        __builtin_amdgcn_readfirstlane(i1.x), __builtin_amdgcn_readfirstlane(i1.y), \
+                        __builtin_amdgcn_readfirstlane(i1.z), __builtin_amdgcn_readfirstlane(i1.w)}; \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                          \
+      const int id = ids[i];                                                                 \
+      if (id != -1) {                                                                        \
+        const uint8_t* src = id >= 0 ? kv_addr(ctx, id) : ctx.win + (int64_t)(-2 - id) * rb;  \
+        __builtin_amdgcn_global_load_lds(                                                    \
+            (const void*)(src + 16 * lane),                                                  \
+            (__attribute__((address_space(3))) void*)&sm.X[BUF][xrow(8 * w + i)][0], 16, 0, 0); \
+      }                                                                                      \
+    }                                                                                        \
+  }
+  if (ntiles > 0) CSA_PF_LOAD(0, 0);
+
+  // ---- queries (B operand of S^T) in registers: RMSNorm over the head (its
+  // four lane groups), RoPE at q, scaled to log2 units, bf16
+  bf16x8 qf[16];
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      float v[8];
+      if (a.q_t == CSA_BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
+          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
+        }
+      } else {
+        load8(qrow, a.q_t, 128 * g + 8 * ks, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float inv = 1.0f / sqrtf(ss / (float)AT_C + a.eps);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const int d0 = 128 * g + 8 * ks;
+      float v[8];
+      if (a.q_t == CSA_BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
+          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
+        }
+      } else {
+        load8(qrow, a.q_t, d0, v);
+      }
+      if (a.q_norm_w != nullptr) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] *= inv * g0[i];
+          v[4 + i] *= inv * g1[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] *= inv;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const int d = d0 + i;
+        if (d >= AT_C - d_r) {
+          const float cs = sm.rcs[(d - (AT_C - d_r)) >> 1][0];
+          const float sn = sm.rcs[(d - (AT_C - d_r)) >> 1][1];
+          const float x0 = v[i], x1 = v[i + 1];
+          v[i] = x0 * cs - x1 * sn;
+          v[i + 1] = x0 * sn + x1 * cs;
+        }
+      }
+      u32x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2_hw(v[2 * i] * qscale, v[2 * i + 1] * qscale);
+      qf[ks] = __builtin_bit_cast(bf16x8, pk);
+    }
+  }
+
+  float m_run = kNegBig, l_run = 0.f;
+  f32x4 O[32];
+#pragma unroll
+  for (int nd = 0; nd < 32; ++nd) O[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // transpose-read addresses: lane (g, q = li) reads entry 8g + 4h + li/4,
+  // dims 16nd + 4(li%4) .. +3
+  const int tr_r0 = xrow(8 * g + (li >> 2)), tr_r1 = xrow(8 * g + 4 + (li >> 2));
+  const int tr_c = 4 * (li & 3);
+  for (int t = 0; t < ntiles; ++t) {
+    // this wave's rows of tile t have landed; after the barrier every wave's
+    // have, and every wave is done with tile t-1, whose buffer takes tile t+1
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (t + 1 < ntiles) CSA_PF_LOAD(t + 1, (t + 1) & 1);
+    CSA_TILE(t, t & 1, 2, 4);
+  }
+#undef CSA_PF_LOAD
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  attend_store_out(a, row, head, g, O, m_run, l_tot, sm.rcs);
+}
+#undef CSA_TILE
 
 // merge split partials in split order, add the sink, normalise, inverse RoPE;
 // one block per (query row, head), one thread per channel pair
@@ -766,6 +963,14 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s) {
   }
   int chunk, nsplit;
   plan_splits(a, &chunk, &nsplit);
+  if (nsplit == 1 && a.kv_t == CSA_BF16 && a.rope_dims <= PF_ROPE_MAX) {
+    // one block per (query row, 64 heads), two resident per compute unit
+    const int64_t nb = (int64_t)rows * (a.nh / 64);
+    const int per_xcd = (int)((nb + 7) / 8);
+    hipLaunchKernelGGL(attend_pf_kernel, dim3((unsigned)(8 * (int64_t)per_xcd)), dim3(256), 0, s, a, rt,
+                       per_xcd);
+    return hipGetLastError();
+  }
   // rows rounded up to a multiple of 8 for the XCD-aware block order
   const int64_t rows8 = (rows + 7) / 8 * 8;
   dim3 grid((unsigned)((int64_t)nsplit * (a.nh / 64) * rows8));
