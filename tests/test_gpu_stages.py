@@ -352,6 +352,37 @@ def test_attend_decode_vs_oracle(name, lengths):
         assert err <= 2e-2
 
 
+@pytest.mark.parametrize("k,lengths,holes,qf32", [
+    (64, [4100, 9000, 300], 0.1, False),   # 192 slots: one block per row, no split
+    (128, [1, 5, 130, 4096], 0.5, False),  # window crossing position 0, half-empty selections
+    (100, [4100, 777], 0.0, True),         # fp32 queries; k not a multiple of the 32-slot tile
+])
+def test_attend_unsplit_rows_vs_oracle(k, lengths, holes, qf32):
+    """Slot lists short enough to stay whole (at most 256 slots with one query
+    per sequence, or any list of a prefill) take the kernel that runs two
+    blocks per compute unit and loads rows straight into shared memory."""
+    d = dev()
+    sp = I.CONFIGS["decode_64k"].replace(B=len(lengths), k=k)
+    inp = I.decode_inputs(sp, seed=340 + k, lengths=lengths)
+    rng = np.random.default_rng(341 + k)
+    nv = np.array([O.n_visible(int(inp["q_pos"][b, 0]), sp.m, int(inp["n_entries"][b]))
+                   for b in range(sp.B)])
+    idx = I.random_index_sets(rng, nv, k, holes=holes)
+    if holes >= 0.5:
+        idx[1, :] = -1                      # one sequence with the window only
+    g = G.upload_decode(inp, d)
+    if qf32:
+        g.q = torch.from_numpy(np.ascontiguousarray(inp["q"], dtype=np.float32)).reshape(g.q.shape).to(d)
+    G.decode_attend(g, idx=torch.from_numpy(idx).reshape(sp.B, 1, k).to(d))
+    torch.cuda.synchronize()
+    out = np64(g.out)
+    for b in range(sp.B):
+        want = OP.decode_attend(inp, b, idx[b])
+        err = np.abs(out[b, 0] - want).max()
+        report("attend unsplit", k=k, b=b, max_abs=err)
+        assert err <= 2e-2
+
+
 def test_attend_window_edges_and_empty_selection():
     """Window crossing position 0, all-empty selections (window only), one row."""
     d = dev()
