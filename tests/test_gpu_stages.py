@@ -287,10 +287,12 @@ def _score_rows(rng, kind, rows, N):
         return rng.integers(-2, 3, size=(rows, N)).astype(np.float32)
     if kind == "bf16":
         return I.cast(rng.standard_normal((rows, N)).astype(np.float32) * 0.5, "bf16")
+    if kind == "bf16ties":  # integers, exact in bf16: equal keys across many slices
+        return rng.integers(-40, 41, size=(rows, N)).astype(np.float32)
     return rng.standard_normal((rows, N)).astype(np.float32)
 
 
-@pytest.mark.parametrize("kind", ["ties", "ties81", "ties5", "bf16", "normal"])
+@pytest.mark.parametrize("kind", ["ties", "ties81", "ties5", "bf16", "bf16ties", "normal"])
 @pytest.mark.parametrize("N,k,m", [(16384, 1024, 4), (3000, 1024, 4), (700, 32, 4),
                                    (1025, 1024, 4), (40000, 512, 4), (20001, 100, 4),
                                    (262144, 1024, 4)])
@@ -304,7 +306,7 @@ def test_topk_bit_exact(kind, N, k, m):
     # query positions: full, ragged, tiny (N(q) <= k), empty
     qpos = np.array([4 * N - 1, 4 * N - 3, 4 * (N // 3) + 2, 4 * k + 1, 4 * k + 7, 2], np.int32)
     n_ent = np.full(rows, N, np.int32)
-    fmt = L.BF16 if kind == "bf16" else L.F32
+    fmt = L.BF16 if kind.startswith("bf16") else L.F32
     dt = torch.bfloat16 if fmt == L.BF16 else torch.float32
     st = torch.from_numpy(S).to(d).to(dt).reshape(rows, 1, N)
     idx = torch.empty(rows, 1, k, dtype=torch.int32, device=d)
