@@ -78,6 +78,22 @@ __device__ __forceinline__ i32x8 widen(u32x4 v) {
   return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
 }
 
+// Head sums of two 16-entry groups.  part0 / part1 are this lane's partial
+// sums (heads 16mt + 4kg + r) for group A / B; the four 16-lane rows (kg) are
+// added with two lane swaps on the VALU.  The 16-lane swap exchanges odd rows
+// of the first operand with even rows of the second: rows become (A: kg 0+1,
+// B: kg 0+1, A: kg 2+3, B: kg 2+3); the 32-lane swap then adds the upper half
+// to the lower.  Lane l < 32 returns the score of entry l of the 32 (A's 16,
+// then B's).
+__device__ __forceinline__ float head_sum_pair(float part0, float part1) {
+  const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(part0), __float_as_uint(part1),
+                                                 false, false);
+  const float t = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false,
+                                                 false);
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
+}
+
 // One block = 4 waves over a contiguous entry range of one query row.  The
 // contraction uses 16x16 matrix-core tiles: 4 tiles of 16 heads (M) by 16
 // entries (N).  Lane (col, kg) = (lane % 16, lane / 16) holds entry col; the
@@ -221,17 +237,8 @@ __global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
           for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
         part[h] = sc;
       }
-      // Sum the four 16-lane rows (kg) of both groups with two lane swaps on
-      // the VALU.  The 16-lane swap exchanges odd rows of the first operand
-      // with even rows of the second: rows become (g0: kg 0+1, g1: kg 0+1,
-      // g0: kg 2+3, g1: kg 2+3); the 32-lane swap then adds the upper half to
-      // the lower, so lane l < 32 ends with the score of entry 16 gp + l.
-      const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[0]),
-                                                     __float_as_uint(part[1]), false, false);
-      const float t = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-      const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
-                                                     false, false);
-      const float sc = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      // lane l < 32: the score of entry 16 gp + l
+      const float sc = head_sum_pair(part[0], part[1]);
       const int n = base + 16 * gp + lane;
       if (lane < 32 && n < e1) {
         if (score_bf16)
@@ -336,29 +343,35 @@ __global__ __launch_bounds__(64 * R) void indexer_rows_kernel(
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
-#pragma unroll 2
-    for (int gi = 0; gi < IR_CH / 16; ++gi) {
+    // two 16-entry groups per step (entries past the row are staged copies of
+    // entry 0: scored, never stored)
+    for (int gi = 0; gi < IR_CH / 16; gi += 2) {
       const int n0 = c * IR_CH + 16 * gi;
       if (n0 >= nv) break;
-      f32x4 acc[4];
+      float part[2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < 2; ++h) {
+        f32x4 acc[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&K[buf][16 * gi + col][32 * ks + 8 * kg]);
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 bk =
+              *reinterpret_cast<const bf16x8*>(&K[buf][16 * (gi + h) + col][32 * ks + 8 * kg]);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][ks], bk, acc[mt], 0, 0, 0);
+        }
+        float sc = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[mt][ks], bk, acc[mt], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
+        part[h] = sc;
       }
-      float sc = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
-      sc += __shfl_xor(sc, 16);
-      sc += __shfl_xor(sc, 32);
-      const int n = n0 + col;
-      if (kg == 0 && n < nv) {
+      const float sc = head_sum_pair(part[0], part[1]);
+      const int n = n0 + lane;
+      if (lane < 32 && n < nv) {
         const int64_t o = (int64_t)row * Nmax + n;
         if (score_bf16)
           reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(sc);
@@ -443,27 +456,32 @@ __global__ __launch_bounds__(64 * R) void indexer_rows_mx_kernel(
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     const int buf = c & 1;
-#pragma unroll 2
-    for (int gi = 0; gi < IRX_CH / 16; ++gi) {
+    // two 16-entry groups per step (entries past the row are staged copies of
+    // entry 0: scored, never stored)
+    for (int gi = 0; gi < IRX_CH / 16; gi += 2) {
       const int n0 = c * IRX_CH + 16 * gi;
       if (n0 >= nv) break;
-      const i32x8 bk = widen(*reinterpret_cast<const u32x4*>(&Kc[buf][16 * gi + col][16 * kg]));
-      const int bs = (int)(Ks[buf][16 * gi + col] >> (8 * kg));
-      f32x4 acc[4];
+      float part[2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(aq[mt]), bk,
-                                                                   f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4,
-                                                                   0, asc[mt], 0, bs);
-      float sc = 0.f;
+      for (int h = 0; h < 2; ++h) {
+        const i32x8 bk =
+            widen(*reinterpret_cast<const u32x4*>(&Kc[buf][16 * (gi + h) + col][16 * kg]));
+        const int bs = (int)(Ks[buf][16 * (gi + h) + col] >> (8 * kg));
+        f32x4 acc[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              widen(aq[mt]), bk, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, asc[mt], 0, bs);
+        float sc = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
-      sc += __shfl_xor(sc, 16);
-      sc += __shfl_xor(sc, 32);
-      const int n = n0 + col;
-      if (kg == 0 && n < nv) {
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sc = fmaf(wr[mt][q], relu_mfma(acc[mt][q]), sc);
+        part[h] = sc;
+      }
+      const float sc = head_sum_pair(part[0], part[1]);
+      const int n = n0 + lane;
+      if (lane < 32 && n < nv) {
         const int64_t o = (int64_t)row * Nmax + n;
         if (score_bf16)
           reinterpret_cast<uint16_t*>(scores)[o] = (uint16_t)f32_to_bf16(sc);
