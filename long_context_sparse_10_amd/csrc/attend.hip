@@ -20,9 +20,10 @@
 //    per-split (m, l) and O / l (bf16) and attend_combine_kernel merges the
 //    splits in order.  Used for FP8 rows and for split slot lists (decode):
 //    its register ring keeps four tiles in flight per block.
-//  * attend_pf_kernel     -- the same math for bf16 rows when the slot list is
-//    not split (prefill, short lists): 256-thread blocks, two per compute
-//    unit, each wave loading its own rows straight into shared memory.
+//  * attend_pf_kernel     -- the same math for bf16 rows and bf16 queries when
+//    the slot list is not split (prefill, short lists): 256-thread blocks, two
+//    per compute unit, each wave loading its own rows straight into shared
+//    memory.
 //  * attend_generic_kernel -- any shape / fp32: one wave per head, VALU.
 #include "common.hpp"
 #include "internal.hpp"
@@ -682,7 +683,7 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
 }
 
 // ============================================================ MFMA, two blocks per CU
-// Many query rows over bf16 rows (prefill, and short lists): one 256-thread
+// Many query rows over bf16 rows with bf16 queries (prefill, and short lists): one 256-thread
 // block per (query row, 64 heads) over the whole slot list, two blocks
 // resident per compute unit.  Each of the 4 waves owns 16 heads and also
 // gathers 8 rows of every tile, straight into shared memory (global_load_lds,
@@ -721,13 +722,6 @@ __global__ __launch_bounds__(256, 2) void attend_pf_kernel(AttendArgs a, Rope rt
   const int ntiles = (total + AT_TILE - 1) / AT_TILE;
   const int64_t rb = ctx.rb;
 
-  // ---- raw query dims 128g .. 128g+127 of this lane's head, issued first
-  const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)row * a.nh + head) * row_bytes(a.q_t, AT_C, 0);
-  u32x4 qraw[16];
-  if (a.q_t == CSA_BF16) {
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 2 * (128 * g + 8 * ks));
-  }
   // ---- slot table and per-tile validity masks, RoPE angles, zeroed tiles
   for (int i = tid; i < ((ntiles * AT_TILE + 63) & ~63); i += 256) {
     const int id = (i < total) ? slot_row_id(ctx, i) : -1;
@@ -770,22 +764,23 @@ __global__ __launch_bounds__(256, 2) void attend_pf_kernel(AttendArgs a, Rope rt
   }
   if (ntiles > 0) CSA_PF_LOAD(0, 0);
 
-  // ---- queries (B operand of S^T) in registers: RMSNorm over the head (its
-  // four lane groups), RoPE at q, scaled to log2 units, bf16
+  // ---- queries (B operand of S^T) in registers: raw dims 128g .. 128g+127 of
+  // this lane's head, RMSNorm over the head (its four lane groups), RoPE at q,
+  // scaled to log2 units, bf16
+  const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)row * a.nh + head) * row_bytes(a.q_t, AT_C, 0);
+  u32x4 qraw[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 2 * (128 * g + 8 * ks));
   bf16x8 qf[16];
   {
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       float v[8];
-      if (a.q_t == CSA_BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
-          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
-        }
-      } else {
-        load8(qrow, a.q_t, 128 * g + 8 * ks, v);
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
+        v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
@@ -797,14 +792,10 @@ __global__ __launch_bounds__(256, 2) void attend_pf_kernel(AttendArgs a, Rope rt
     for (int ks = 0; ks < 16; ++ks) {
       const int d0 = 128 * g + 8 * ks;
       float v[8];
-      if (a.q_t == CSA_BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
-          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
-        }
-      } else {
-        load8(qrow, a.q_t, d0, v);
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(qraw[ks][i] << 16);
+        v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);
       }
       if (a.q_norm_w != nullptr) {
         const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.q_norm_w + d0);
@@ -963,7 +954,7 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s) {
   }
   int chunk, nsplit;
   plan_splits(a, &chunk, &nsplit);
-  if (nsplit == 1 && a.kv_t == CSA_BF16 && a.rope_dims <= PF_ROPE_MAX) {
+  if (nsplit == 1 && a.kv_t == CSA_BF16 && a.q_t == CSA_BF16 && a.rope_dims <= PF_ROPE_MAX) {
     // one block per (query row, 64 heads), two resident per compute unit
     const int64_t nb = (int64_t)rows * (a.nh / 64);
     const int per_xcd = (int)((nb + 7) / 8);

@@ -357,12 +357,14 @@ def test_attend_decode_vs_oracle(name, lengths):
 @pytest.mark.parametrize("k,lengths,holes,qf32", [
     (64, [4100, 9000, 300], 0.1, False),   # 192 slots: one block per row, no split
     (128, [1, 5, 130, 4096], 0.5, False),  # window crossing position 0, half-empty selections
-    (100, [4100, 777], 0.0, True),         # fp32 queries; k not a multiple of the 32-slot tile
+    (100, [4100, 777], 0.0, False),        # k not a multiple of the 32-slot tile
+    (100, [4100, 777], 0.0, True),         # fp32 queries: the single-block kernel, unsplit
 ])
 def test_attend_unsplit_rows_vs_oracle(k, lengths, holes, qf32):
     """Slot lists short enough to stay whole (at most 256 slots with one query
-    per sequence, or any list of a prefill) take the kernel that runs two
-    blocks per compute unit and loads rows straight into shared memory."""
+    per sequence, or any list of a prefill) take, with bf16 queries, the kernel
+    that runs two blocks per compute unit and loads rows straight into shared
+    memory."""
     d = dev()
     sp = I.CONFIGS["decode_64k"].replace(B=len(lengths), k=k)
     inp = I.decode_inputs(sp, seed=340 + k, lengths=lengths)
