@@ -234,6 +234,115 @@ __global__ __launch_bounds__(256, 2) void oproj_tiled_kernel(
     }
 }
 
+
+// C tile 256 x 256 per 256-thread block, one block per CU and one wave per
+// SIMD: wave w owns rows 128 (w / 2) .. +127 and columns 128 (w % 2) .. +127 as
+// 4 x 4 tiles of v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane (in
+// the accumulation registers: one wave per SIMD may use 512 registers).  Every
+// 16-byte operand read from LDS feeds four matrix-core instructions: 16 B of
+// LDS per lane per 32x32x16 instruction, half the 256 x 128 kernel's, and half
+// its global traffic per flop.  Same K-step, staging and XCD order otherwise.
+constexpr int OB_M = 256, OB_N = 256, OB_K = 64, OB_LD = OB_K + 8;
+
+__global__ __launch_bounds__(256, 1) void oproj_big_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int64_t a_goff, const uint16_t* __restrict__ W,
+    int64_t w_gstride, void* __restrict__ C, int64_t ldc, int64_t c_goff, int c_bf16, int M, int N,
+    int K) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][OB_M][OB_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][OB_N][OB_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nN = (N + OB_N - 1) / OB_N, nM = (M + OB_M - 1) / OB_M;
+  const int per_grp = (nM + 7) / 8 * 8 * nN;
+  const int grp = blockIdx.x / per_grp, L = blockIdx.x % per_grp;
+  const int mt = (L / 8 / nN) * 8 + (L & 7), nt = (L / 8) % nN;
+  if (mt >= nM) return;
+  const int m0 = mt * OB_M, n0 = nt * OB_N;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const uint16_t* Ag = A + grp * a_goff;
+  const uint16_t* Wg = W + grp * w_gstride;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  // per K-step: A and W 256 x 64 each = 2048 chunks of 8 (8 per thread each)
+  u32x4 ra[8], rw[8];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int idx = tid + 256 * p, r = idx >> 3, kc = (idx & 7) * 8;
+      ra[p] = m0 + r < M ? *reinterpret_cast<const u32x4*>(Ag + (int64_t)(m0 + r) * lda + k0 + kc)
+                         : u32x4{0u, 0u, 0u, 0u};
+      rw[p] = n0 + r < N ? *reinterpret_cast<const u32x4*>(Wg + (int64_t)(n0 + r) * K + k0 + kc)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int idx = tid + 256 * p;
+      *reinterpret_cast<u32x4*>(&As[b][idx >> 3][(idx & 7) * 8]) = ra[p];
+      *reinterpret_cast<u32x4*>(&Ws[b][idx >> 3][(idx & 7) * 8]) = rw[p];
+    }
+  };
+  const int nk = K / OB_K;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load((kt + 1) * OB_K);
+    // operand fragments of sub-step ks + 1 are read while ks multiplies
+    bf16x8 af[2][4], wf[2][4];
+    auto frags = [&](int ks, int fb) {
+      const int kof = 16 * ks + 8 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[fb][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&As[cur][wm + 32 * i + (lane & 31)][kof]));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wf[fb][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&Ws[cur][wn + 32 * j + (lane & 31)][kof]));
+    };
+    frags(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < OB_K / 16; ++ks) {
+      if (ks + 1 < OB_K / 16) frags(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], wf[ks & 1][j], acc[i][j], 0, 0, 0);
+      if (ks + 1 < OB_K / 16) {
+        // the next fragments' 8 reads spread over this sub-step's 16 products
+        _Pragma("unroll") for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+      }
+    }
+    if (kt + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+  // D: lane holds column l%32, rows 8(r/4) + 4(l/32) + r%4 of each 32 x 32 tile
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gn = n0 + wn + 32 * j + (lane & 31);
+      if (gn >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gm = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (gm >= M) continue;
+        const int64_t o = (int64_t)gm * ldc + grp * c_goff + gn;
+        if (c_bf16)
+          reinterpret_cast<uint16_t*>(C)[o] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+        else
+          reinterpret_cast<float*>(C)[o] = acc[i][j][r];
+      }
+    }
+}
+
 // =============================================================== fp32 operands
 __global__ __launch_bounds__(256) void oproj_generic_kernel(
     const float* __restrict__ A, int64_t lda, int64_t a_goff, const float* __restrict__ W,
@@ -288,6 +397,11 @@ static hipError_t launch_oproj_gemm(const void* A, int64_t lda, int64_t a_goff, 
     const int64_t count = p_split;  // M * ldc, a multiple of 4
     hipLaunchKernelGGL(oproj_reduce_kernel, dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0,
                        s, (const float*)part, p_split, splits, C, c_bf16, count);
+  } else if (M >= OB_M && N >= OB_N && K % OB_K == 0) {
+    const int64_t nN = (N + OB_N - 1) / OB_N, nM = (M + OB_M - 1) / OB_M;
+    dim3 grid((unsigned)((nM + 7) / 8 * 8 * nN * groups));
+    hipLaunchKernelGGL(oproj_big_kernel, grid, dim3(256), 0, s, (const uint16_t*)A, lda, a_goff,
+                       (const uint16_t*)W, w_gstride, C, ldc, (int64_t)N, c_bf16, M, N, K);
   } else {
     const int64_t nN = (N + OT_N - 1) / OT_N, nM = (M + OT_M - 1) / OT_M;
     dim3 grid((unsigned)((nM + 7) / 8 * 8 * nN * groups));
