@@ -104,18 +104,18 @@ __device__ __forceinline__ float head_sum_pair(float part0, float part1) {
 //  * MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4, one instruction per tile: lane
 //    kg holds code bytes 16kg .. 16kg+15 (dims 32kg .. 32kg+31), exactly the
 //    32-element block whose e8m0 scale the matrix core applies.
-// A wave scores G groups of 16 entries per step (bf16 G = 2, MXFP4 G = 8),
+// A wave scores G groups of 16 entries per step (bf16 G = 2, MXFP4 G = 4),
 // reduces the head sum of two groups at a time across its four lane rows, and
 // keeps a ring of three steps of raw key bytes in registers: two in flight
 // while the third is scored.
 template <bool MX>
-__global__ __launch_bounds__(IDX_WAVES * 64, 2) void indexer_mfma_kernel(
+__global__ __launch_bounds__(IDX_WAVES * 64, MX ? 4 : 2) void indexer_mfma_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ kI,
     const uint8_t* __restrict__ kI_scale, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int Nmax, int m, int ent_per_block,
     void* __restrict__ scores, int score_bf16, PageMap pg) {
-  constexpr int G = MX ? 8 : 2;
+  constexpr int G = MX ? 4 : 2;
   constexpr int64_t RB = MX ? 64 : 256;  // key row bytes
   extern __shared__ __attribute__((aligned(16))) uint32_t sbuf[];  // the block's scores
   const int tiles = (Nmax + ent_per_block - 1) / ent_per_block;
@@ -520,10 +520,15 @@ hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_
                        sbf);
   } else if ((in_t == CSA_BF16 || in_t == CSA_MXFP4) && nI == 64 && cI == 128 &&
              (!pg.paged() || pg.shift >= 4)) {
-    // about two resident blocks per CU over the whole call; a block covers a
-    // multiple of one step of its 4 waves (bf16 128 entries, MXFP4 512)
+    // bf16: about two resident blocks per CU over the whole call; a block
+    // covers a multiple of 512 entries (MXFP4) or 128 (bf16), whole steps of
+    // its 4 waves (bf16 128 entries, MXFP4 256)
     const int step = in_t == CSA_MXFP4 ? 512 : 128;
-    const int64_t want = ((int64_t)Nmax * rows + 511) / 512;
+    // MXFP4 keys carry more VALU work per byte (the epilogue outweighs the
+    // matrix core): four waves per SIMD (128 VGPRs) and about four blocks per
+    // CU hide it better than two
+    const int64_t want = in_t == CSA_MXFP4 ? ((int64_t)Nmax * rows + 1023) / 1024
+                                           : ((int64_t)Nmax * rows + 511) / 512;
     int epb = (int)(((want + step - 1) / step) * step);
     epb = epb < 2 * step ? 2 * step : (epb > 8192 ? 8192 : epb);
     dim3 grid((unsigned)(((int64_t)Nmax + epb - 1) / epb * rows));
