@@ -40,27 +40,13 @@ METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP
 # of known size (--copy-probe).  An entry holds for the kernel source it was
 # taken on (sha256 of the .hip file); after any change it reports null.
 TRAFFIC = {
-    "decode_64k": dict(src="indexer.hip", sha256="b66562989b06ce07e808673a2482c3da4cb9f380f4136657f0f3460d2d780dfc",
-                fetch_kib=67679.0, write_kib=2048.7, fetch_scale=1.9998,
-                write_scale=1.0),
-    "hca_decode_1m": dict(src="attend.hip", sha256="79509f3f90e2cfeeeca7b7ea2837c98a6cf270d73033536a1f08942abaea2899",
-                fetch_kib=75783.5, write_kib=17536.0, fetch_scale=1.9998,
-                write_scale=1.0),
-    "decode_1m_fp4": dict(src="indexer.hip", sha256="b66562989b06ce07e808673a2482c3da4cb9f380f4136657f0f3460d2d780dfc",
-                fetch_kib=69948.8, write_kib=4096.1, fetch_scale=1.9998,
-                write_scale=1.0),
-    "prefill_32k": dict(src="attend.hip", sha256="79509f3f90e2cfeeeca7b7ea2837c98a6cf270d73033536a1f08942abaea2899",
-                fetch_kib=3294813.5, write_kib=2097203.4, fetch_scale=1.9998,
-                write_scale=1.0),
-    "prefill_32k_mxfp4": dict(src="attend.hip", sha256="79509f3f90e2cfeeeca7b7ea2837c98a6cf270d73033536a1f08942abaea2899",
-                fetch_kib=3304052.0, write_kib=2097216.0, fetch_scale=1.9998,
-                write_scale=1.0),
-    "oproj_decode": dict(src="oproj.hip", sha256="233800c0b523f5652c1ca82c87ce43f04b49013854953988b76bc4eeb6b99009",
-                fetch_kib=80947.3, write_kib=8970.1, fetch_scale=1.9998,
-                write_scale=1.0),
-    "oproj_prefill": dict(src="oproj.hip", sha256="233800c0b523f5652c1ca82c87ce43f04b49013854953988b76bc4eeb6b99009",
-                fetch_kib=6491159.2, write_kib=806256.8, fetch_scale=1.9998,
-                write_scale=1.0),
+    'decode_1m_fp4': {"src": "indexer.hip", "sha256": "b40a9843a92fa8434d9007e0a6b3a4175e895ba9243b377d30d44c541c167ff1", "fetch_kib": 69869.3, "write_kib": 4096.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'decode_64k': {"src": "indexer.hip", "sha256": "b40a9843a92fa8434d9007e0a6b3a4175e895ba9243b377d30d44c541c167ff1", "fetch_kib": 67677.5, "write_kib": 2048.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'hca_decode_1m': {"src": "attend.hip", "sha256": "6602ef04591644406c8bc08161f432c5397dc461c47617c3322c90d551bf9ed3", "fetch_kib": 75784.7, "write_kib": 17536.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'oproj_decode': {"src": "oproj.hip", "sha256": "99d8386e33f20e6b4550c52e1cad5985505842be7148f54ce0c4b5e890c9f760", "fetch_kib": 80948.4, "write_kib": 8967.4, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'oproj_prefill': {"src": "oproj.hip", "sha256": "99d8386e33f20e6b4550c52e1cad5985505842be7148f54ce0c4b5e890c9f760", "fetch_kib": 4553178.6, "write_kib": 842469.5, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'prefill_32k': {"src": "attend.hip", "sha256": "6602ef04591644406c8bc08161f432c5397dc461c47617c3322c90d551bf9ed3", "fetch_kib": 3203646.0, "write_kib": 2097152.1, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'prefill_32k_mxfp4': {"src": "attend.hip", "sha256": "6602ef04591644406c8bc08161f432c5397dc461c47617c3322c90d551bf9ed3", "fetch_kib": 3204056.8, "write_kib": 2097153.0, "fetch_scale": 1.9998, "write_scale": 1.0},
 }
 
 
