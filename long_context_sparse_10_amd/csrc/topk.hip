@@ -168,13 +168,16 @@ __device__ __forceinline__ int wave_scan_excl(int v, int* total) {
 // small buffer keeps more rows resident per CU when many short rows run
 constexpr int TK_CAND_CAP = 2048;
 
-template <bool BF16>
+// W1: width of the first digit of fp32 keys (13, or 12 when many rows share the
+// GPU: a 16 KB histogram lets four 512-thread blocks reside per CU instead of
+// three).  bf16 keys take 10 then 6 bits.
+template <bool BF16, int W1>
 __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ scores,
                                                     const int32_t* __restrict__ q_pos,
                                                     const int32_t* __restrict__ n_entries, int Tq,
                                                     int Nmax, int m, int k, int vec,
                                                     int32_t* __restrict__ idx) {
-  __shared__ int hist[BF16 ? 1024 : 8192];
+  __shared__ int hist[BF16 ? 1024 : (1 << W1)];
   extern __shared__ uint32_t cand[];  // [min(16 * blockDim, TK_CAND_CAP)]: keys sharing the k-th's first digit
   __shared__ int scan_ws[16];
   __shared__ uint32_t sh_digit;
@@ -199,10 +202,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
 #pragma unroll
     for (int i = 0; i < 16; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
   }
-  // ---- first digit, block-wide: 13 bits of fp32 keys (bits 31..19), 10 of bf16
-  // (15..6); wide digits spread the clustered score exponents over many bins
-  constexpr int SH1 = BF16 ? 6 : 19;
-  constexpr int NB1 = 1 << (BF16 ? 10 : 13);
+  // ---- first digit, block-wide: W1 bits of fp32 keys (bits 31..32-W1), 10 of
+  // bf16 (15..6); wide digits spread the clustered score exponents over many bins
+  constexpr int SH1 = BF16 ? 6 : 32 - W1;
+  constexpr int NB1 = 1 << (BF16 ? 10 : W1);
   for (int i = tid; i < NB1; i += nt) hist[i] = 0;
   if (tid == 0) sh_ncand = 0;
   __syncthreads();
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
     uint32_t prefix = d1 << SH1, pmask = ~0u << SH1;
     int shift = SH1;
     while (shift > 0) {
-      const int width = BF16 ? 6 : (shift == 19 ? 10 : 9);
+      const int width = BF16 ? 6 : min(shift, 10);
       shift -= width;
       const int nbins = 1 << width;
       const uint32_t dmask = (uint32_t)nbins - 1u;
@@ -263,11 +266,11 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
     }
   } else if (tid < 64) {
     // ---- remaining digits over the candidates by wave 0 alone (no block barriers):
-    // fp32 keys 10 + 9 bits (18..9, 8..0), bf16 keys 6 bits (5..0)
+    // fp32 keys 10 + 9 (W1 13) or 10 + 10 bits (W1 12), bf16 keys 6 bits (5..0)
     uint32_t prefix = d1 << SH1, pmask = ~0u << SH1;
     int shift = SH1;
     while (shift > 0) {
-      const int width = BF16 ? 6 : (shift == 19 ? 10 : 9);
+      const int width = BF16 ? 6 : min(shift, 10);
       shift -= width;
       const int nbins = 1 << width;
       const uint32_t dmask = (uint32_t)nbins - 1u;
@@ -578,11 +581,16 @@ hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_p
   int threads = 64;  // the smallest power of two >= Nmax / 16, at least one wave
   while (threads * 16 < Nmax) threads *= 2;
   const size_t cand_bytes = (size_t)(16 * threads < TK_CAND_CAP ? 16 * threads : TK_CAND_CAP) * sizeof(uint32_t);
+  // more rows than compute units: occupancy counts more than a row's latency
+  // (the selection is exact either way)
   if (bf)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3(rows), dim3(threads), cand_bytes, s, scores,
+    hipLaunchKernelGGL((topk_kernel<true, 13>), dim3(rows), dim3(threads), cand_bytes, s, scores,
+                       q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
+  else if (rows > 256)
+    hipLaunchKernelGGL((topk_kernel<false, 12>), dim3(rows), dim3(threads), cand_bytes, s, scores,
                        q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(rows), dim3(threads), cand_bytes, s, scores,
+    hipLaunchKernelGGL((topk_kernel<false, 13>), dim3(rows), dim3(threads), cand_bytes, s, scores,
                        q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
   return hipGetLastError();
 }

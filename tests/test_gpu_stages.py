@@ -321,6 +321,30 @@ def test_topk_bit_exact(kind, N, k, m):
         np.testing.assert_array_equal(got[r], want, err_msg=f"row {r} nv {nv}")
 
 
+@pytest.mark.parametrize("kind", ["ties", "ties5", "normal"])
+@pytest.mark.parametrize("N,k", [(3000, 1024), (9000, 1024), (700, 32)])
+def test_topk_many_rows_bit_exact(kind, N, k):
+    """More rows than compute units take the fp32 kernel with a 12-bit first
+    digit (four blocks per CU); the index sets must still match the oracle
+    exactly, ties and the candidate-buffer overflow included."""
+    d = dev()
+    m, rows = 4, 300
+    rng = np.random.default_rng(7 * N + k)
+    S = _score_rows(rng, kind, rows, N)
+    qpos = rng.integers(0, 4 * N + 8, size=rows).astype(np.int32)   # ragged, some short
+    qpos[:3] = [4 * N - 1, 2, 4 * k + 1]
+    n_ent = np.full(rows, N, np.int32)
+    st = torch.from_numpy(S).to(d).reshape(rows, 1, N)
+    idx = torch.empty(rows, 1, k, dtype=torch.int32, device=d)
+    L.topk_select(st, L.F32, torch.from_numpy(qpos).reshape(rows, 1).to(d),
+                  torch.from_numpy(n_ent).to(d), rows, 1, N, m, k, idx)
+    got = idx.cpu().numpy()[:, 0]
+    for r in range(rows):
+        nv = int(O.n_visible(int(qpos[r]), m, N))
+        want = O.topk(S[r].astype(np.float64), nv, k)
+        np.testing.assert_array_equal(got[r], want, err_msg=f"row {r} nv {nv}")
+
+
 # =================================================================== attention
 def _attend_case(name, lengths, seed, holes=0.1, n_win=None):
     sp = I.CONFIGS[name].replace(B=len(lengths))
