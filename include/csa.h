@@ -205,7 +205,9 @@ csa_status indexer_score(const void* qI, const uint8_t* qI_scale, csa_dtype qI_t
  *
  *  scores  [B, Tq, Nmax] in score_t (CSA_F32 or CSA_BF16); only s < N(q) read.
  *  idx     [B, Tq, k] int32.
- *  ws      not used by the current kernels (size 0), kept for the protocol.
+ *  ws      int32 scratch for rows of more than 16,384 entries (per-slice
+ *          digit histograms, row state and slice counts; workspace protocol
+ *          above); size 0 for shorter rows.
  */
 csa_status topk_select(const void* scores, csa_dtype score_t,
                        const int32_t* q_pos, const int32_t* n_entries,
@@ -234,7 +236,9 @@ csa_status topk_select(const void* scores, csa_dtype score_t,
  *          win_len = T, one row per token).  win may be NULL iff n_win == 0.
  *  sink    [nh] fp32 logits z'_h (not multiplied by scale).
  *  out     [B, Tq, nh, c] in out_t (CSA_F32 / CSA_BF16).
- *  ws      fp32 split-softmax partials (workspace protocol above).
+ *  ws      split-softmax partials (workspace protocol above): O / l in bf16 and
+ *          (m, l) in fp32 per (query row, split, head); size 0 when the slot
+ *          lists are not split (many query rows, or at most 256 slots).
  */
 csa_status sparse_mqa_attend(const void* q, csa_dtype q_t, const float* q_norm_w, float eps,
                              int rope_dims, float rope_theta, const int32_t* q_pos,
