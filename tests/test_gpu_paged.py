@@ -62,6 +62,30 @@ def test_paged_decode_step_equals_dense(name, lengths):
            pages=int(pool.pool.shape[0]), equal=True)
 
 
+def test_paged_unsplit_attention_equals_dense():
+    """Slot lists that stay whole (64 selected + 128 window slots) take the
+    two-blocks-per-CU attention kernel, whose waves load rows straight into
+    shared memory through the page table: same bits as the dense cache."""
+    d = dev()
+    k, lengths = 64, [65536, 40003, 7000]
+    sp = I.CONFIGS["decode_64k"].replace(B=len(lengths), k=k)
+    inp = I.decode_inputs(sp, seed=707, lengths=lengths)
+    rng = np.random.default_rng(708)
+    nv = np.array([O.n_visible(int(inp["q_pos"][b, 0]), sp.m, int(inp["n_entries"][b]))
+                   for b in range(sp.B)])
+    it = torch.from_numpy(I.random_index_sets(rng, nv, k, holes=0.2)).reshape(sp.B, 1, k).to(d)
+    g = G.upload_decode(inp, d)
+    G.decode_attend(g, idx=it)
+    torch.cuda.synchronize()
+    want = g.out.clone()
+    pool = G.page_decode(g, seed=19)
+    g.out.fill_(float("nan"))
+    G.decode_attend(g, idx=it)
+    torch.cuda.synchronize()
+    assert torch.equal(g.out, want)
+    report("paged unsplit attention", k=k, lengths=lengths, pages=int(pool.pool.shape[0]), equal=True)
+
+
 def _tiny_pool(sp, n, p, d):
     """Hybrid pool for a tiny prefill: a CSA config fills the CSA sections, an
     HCA config the HCA section (one entry per page)."""
