@@ -697,6 +697,16 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
 constexpr int PF_ROPE_MAX = 64;  // RoPE dims (the rotation table is sized for these)
 constexpr int PF_CHUNK = 16;     // (row, head group) items per XCD run
 
+// One wave copies a 1 KB row into shared memory: lane l's 16 bytes at src go
+// to shared address dst + 16 l (global_load_lds_dwordx4, M0 = dst).  Written as asm, which
+// has no output registers, so that the compiler does not track the copy: it
+// cannot tell which tile a copy writes, and would otherwise wait for every
+// copy in flight before each transpose read of the other tile.  The kernel
+// orders the copies itself (vmcnt(0) and a barrier before a tile is read).
+__device__ __forceinline__ void pf_gather_row(const uint8_t* src, uint32_t dst) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+}
+
 struct AttendPfSmem {
   uint16_t X[2][AT_TILE][AT_LDX];  // gathered rows (double-buffered tiles), rows permuted by xrow
   int32_t slot[AT_TAB + 64];
@@ -746,6 +756,10 @@ __global__ __launch_bounds__(256, 2) void attend_pf_kernel(AttendArgs a, Rope rt
     reinterpret_cast<u32x4*>(&sm.X[0][0][0])[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();  // table, angles and zeroed tiles ready
 
+  // shared address of the tile buffers, and the wave index, as scalars
+  const uint32_t x_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&sm.X[0][0][0]);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   // ---- gather rows 8w .. 8w+7 of tile T into X[BUF]: one 1 KB row per wave
   // instruction, lane l bytes 16l .. 16l+15; slot ids are wave-uniform scalars
 #define CSA_PF_LOAD(T, BUF)                                                                  \
@@ -760,9 +774,8 @@ __global__ __launch_bounds__(256, 2) void attend_pf_kernel(AttendArgs a, Rope rt
       const int id = ids[i];                                                                 \
       if (id != -1) {                                                                        \
         const uint8_t* src = id >= 0 ? kv_addr(ctx, id) : ctx.win + (int64_t)(-2 - id) * rb;  \
-        __builtin_amdgcn_global_load_lds(                                                    \
-            (const void*)(src + 16 * lane),                                                  \
-            (__attribute__((address_space(3))) void*)&sm.X[BUF][xrow(8 * w + i)][0], 16, 0, 0); \
+        pf_gather_row(src + 16 * lane,                                                       \
+                      x_lds + (uint32_t)(((BUF) * AT_TILE + xrow(8 * wu + i)) * (AT_LDX * 2))); \
       }                                                                                      \
     }                                                                                        \
   }
