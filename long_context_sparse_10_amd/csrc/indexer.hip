@@ -120,7 +120,8 @@ __global__ __launch_bounds__(IDX_WAVES * 64, MX ? 4 : 2) void indexer_mfma_kerne
   extern __shared__ __attribute__((aligned(16))) uint32_t sbuf[];  // the block's scores
   const int tiles = (Nmax + ent_per_block - 1) / ent_per_block;
   const int row = blockIdx.x / tiles, b = row / Tq;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index as a scalar: the step loop below is then uniform control flow
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kg = lane >> 4, col = lane & 15;
   const int e0 = (blockIdx.x % tiles) * ent_per_block;
   // dense rows: the first two steps are fetched before the visible-entry
@@ -147,7 +148,11 @@ __global__ __launch_bounds__(IDX_WAVES * 64, MX ? 4 : 2) void indexer_mfma_kerne
         const int gs = __builtin_amdgcn_readfirstlane(base) + 16 * g;
         const int ge = gs < e1 ? gs : e0;
         const int nn = n < e1 ? n : ge;
-        const int64_t pb = (int64_t)pg.page(b, ge) * pg.page_bytes;
+        // the page table does not change during the kernel: read it through
+        // the constant address space, a scalar load at a uniform address
+        const __attribute__((address_space(4))) int32_t* tab =
+            (const __attribute__((address_space(4))) int32_t*)pg.table;
+        const int64_t pb = (int64_t)tab[(int64_t)b * pg.max_blocks + (ge >> pg.shift)] * pg.page_bytes;
         const int sl = nn & ((1 << pg.shift) - 1);
         ko = pb + (int64_t)sl * RB;
         so = pb + (int64_t)sl * 4;
@@ -166,22 +171,8 @@ __global__ __launch_bounds__(IDX_WAVES * 64, MX ? 4 : 2) void indexer_mfma_kerne
       }
     }
   };
-  constexpr int STEP = IDX_WAVES * 16 * G;
-  int base = e0 + wave * 16 * G;
-  Raw r0, r1, r2;
-  if (!pg.paged()) {
-    if (base < e1) fetch(base, r0);
-    if (base + STEP < e1) fetch(base + STEP, r1);
-  }
-  const int nv = min(min(n_entries[b], Nmax), (q_pos[row] + 1) / m);
-  if (e0 >= nv) return;
-  e1 = min(e1, nv);
-  if (pg.paged()) {
-    if (base < e1) fetch(base, r0);
-    if (base + STEP < e1) fetch(base + STEP, r1);
-  }
-
-  // query fragments of head 16*mt + col in the keys' K order
+  // query fragments of head 16*mt + col in the keys' K order (loaded before
+  // the keys, so that their first use waits for none of the key loads)
   bf16x8 afr[4][MX ? 1 : 4];
   u32x4 aq[4];
   int asc[4];
@@ -204,6 +195,26 @@ __global__ __launch_bounds__(IDX_WAVES * 64, MX ? 4 : 2) void indexer_mfma_kerne
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) wr[mt][r] = w[(int64_t)row * 64 + 16 * mt + 4 * kg + r];
+
+  // Every fetch below is unconditional (steps past the range read in-bounds
+  // rows and are not scored): with a fixed number of loads per step, the
+  // compiler's in-order load counts let a step's keys be used while the two
+  // later steps are still in flight.  A fetch under a condition made it
+  // assume the later steps might be absent and wait for all loads instead.
+  constexpr int STEP = IDX_WAVES * 16 * G;
+  int base = e0 + wave * 16 * G;
+  Raw r0, r1, r2;
+  if (!pg.paged()) {
+    fetch(base, r0);
+    fetch(base + STEP, r1);
+  }
+  const int nv = min(min(n_entries[b], Nmax), (q_pos[row] + 1) / m);
+  if (e0 >= nv) return;
+  e1 = min(e1, nv);
+  if (pg.paged()) {
+    fetch(base, r0);
+    fetch(base + STEP, r1);
+  }
 
   auto process = [&](const Raw& r, int base) {
 #pragma unroll
@@ -248,16 +259,25 @@ __global__ __launch_bounds__(IDX_WAVES * 64, MX ? 4 : 2) void indexer_mfma_kerne
       }
     }
   };
-  for (; base < e1; base += 3 * STEP) {
-    if (base + 2 * STEP < e1) fetch(base + 2 * STEP, r2);
+  // every load so far has landed (the first two key steps as well: the first
+  // is needed now and the second left right after it).  With nothing in
+  // flight at its head, the loop's in-order counts cover key steps alone and
+  // each step waits only for its own keys; a partial wait here left the
+  // compiler assuming older loads in flight, and it drained the next step too.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // whole triples of steps, then the last one or two (already in r0, r1);
+  // the loop has no other exit, so no step's loads are thought pending at
+  // its head
+  for (; base + 2 * STEP < e1; base += 3 * STEP) {
+    fetch(base + 2 * STEP, r2);
     process(r0, base);
-    if (base + STEP >= e1) break;
-    if (base + 3 * STEP < e1) fetch(base + 3 * STEP, r0);
+    fetch(base + 3 * STEP, r0);
     process(r1, base + STEP);
-    if (base + 2 * STEP >= e1) break;
-    if (base + 4 * STEP < e1) fetch(base + 4 * STEP, r1);
+    fetch(base + 4 * STEP, r1);
     process(r2, base + 2 * STEP);
   }
+  if (base < e1) process(r0, base);
+  if (base + STEP < e1) process(r1, base + STEP);
   // the block's scores leave once, after the key stream: a store issued
   // between key loads would hold up the in-order wait for the next key step
   __syncthreads();
