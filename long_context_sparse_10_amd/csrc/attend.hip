@@ -547,13 +547,16 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   }
 
   // ---- loader staging: rows 8mw..8mw+7 of a tile, lane l holds dims 8l..8l+7;
-  // all addresses first (empty slots read row 0 and are zeroed at commit)
+  // all addresses first (empty slots read row 0 and are zeroed at commit).
+  // Needs ntiles > 0; a tile past the end re-reads the last tile (it is
+  // never committed).
 #define CSA_STAGE(STG, OK, T)                                                                \
-  if ((T) < ntiles) {                                                                        \
+  {                                                                                          \
     const uint8_t* src[8];                                                                   \
     OK = 0u;                                                                                 \
     {                                                                                        \
-      const int4* sp4 = reinterpret_cast<const int4*>(&sm.slot[(T) * AT_TILE + 8 * mw]);     \
+      const int tc = (T) < ntiles ? (T) : ntiles - 1;                                        \
+      const int4* sp4 = reinterpret_cast<const int4*>(&sm.slot[tc * AT_TILE + 8 * mw]);      \
       const int4 i0 = sp4[0], i1 = sp4[1];                                                   \
       /* every lane read the same ids: scalar copies keep the addresses on the SALU */    \
       const int ids[8] = {__builtin_amdgcn_readfirstlane(i0.x), __builtin_amdgcn_readfirstlane(i0.y), \
@@ -615,24 +618,44 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
     // barrier count matches the math waves': one, then one per tile.
     u32x4 st0[8], st1[8];
     uint32_t ok0 = 0u, ok1 = 0u;
-    CSA_STAGE(st0, ok0, 0);
-    CSA_STAGE(st1, ok1, 1);
-    CSA_QPREP();
-    if (ntiles > 0) CSA_COMMIT(st0, ok0, 0);
-    CSA_STAGE(st0, ok0, 2);
-    __syncthreads();
-#define CSA_PHASE(STG, OK, J)                                                                \
-    if (t + (J) < ntiles) {                                                                  \
-      CSA_COMMIT(STG, OK, (t + (J)) & 1);                                                    \
-      CSA_STAGE(STG, OK, t + (J) + 2);                                                       \
-    }                                                                                        \
-    __syncthreads();                                                                         \
-    if (t + (J) >= ntiles) break;
-    for (int t = 0; t < ntiles; t += 2) {
-      CSA_PHASE(st1, ok1, 1);
-      CSA_PHASE(st0, ok0, 2);
+    if (ntiles > 0) {
+      CSA_STAGE(st0, ok0, 0);
+      CSA_STAGE(st1, ok1, 1);
     }
+    CSA_QPREP();
+    if (ntiles > 0) {
+      CSA_COMMIT(st0, ok0, 0);
+      CSA_STAGE(st0, ok0, 2);
+    }
+    __syncthreads();
+    // phase u (1 .. ntiles): commit tile u (when it exists) from set u % 2,
+    // stage tile u + 2 into that set (when it exists), then the tile barrier.
+    // While every stage is a real tile, phases run in pairs with one loop
+    // exit and a stage in every phase, so each commit waits for its own tile
+    // only; the last phases (at most four) follow with their conditions.
+#define CSA_PHASE(STG, OK, U)                                                                \
+    {                                                                                        \
+      CSA_COMMIT(STG, OK, (U) & 1);                                                          \
+      CSA_STAGE(STG, OK, (U) + 2);                                                           \
+      __syncthreads();                                                                       \
+    }
+#define CSA_LAST_PHASE(STG, OK, U)                                                           \
+    if ((U) <= ntiles) {                                                                     \
+      if ((U) < ntiles) CSA_COMMIT(STG, OK, (U) & 1);                                        \
+      if ((U) + 2 < ntiles) CSA_STAGE(STG, OK, (U) + 2);                                     \
+      __syncthreads();                                                                       \
+    }
+    int u = 1;
+    for (; u + 3 < ntiles; u += 2) {
+      CSA_PHASE(st1, ok1, u);
+      CSA_PHASE(st0, ok0, u + 1);
+    }
+    CSA_LAST_PHASE(st1, ok1, u);
+    CSA_LAST_PHASE(st0, ok0, u + 1);
+    CSA_LAST_PHASE(st1, ok1, u + 2);
+    CSA_LAST_PHASE(st0, ok0, u + 3);
 #undef CSA_PHASE
+#undef CSA_LAST_PHASE
     return;
   }
   float m_run = kNegBig, l_run = 0.f;
