@@ -411,6 +411,54 @@ def test_attend_unsplit_rows_vs_oracle(k, lengths, holes, qf32):
         assert err <= 2e-2
 
 
+@pytest.mark.parametrize("total", [900, 950, 980, 1000, 1100, 1300, 1700, 2000, 2300, 2700, 3000])
+def test_attend_split_tile_counts_vs_oracle(total):
+    """Split slot lists (k + 128 window slots = total) whose splits hold 4 to 12
+    tiles of 32 slots and whose last split holds 1 to 10: every way through
+    the loader ring (phases in pairs while both stages are real tiles, then the
+    last phases with their conditions).  The second sequence sees only half of
+    k entries, so its selections are half empty."""
+    d = dev()
+    k = total - 128
+    sp = I.CONFIGS["decode_64k"].replace(B=2, k=k)
+    inp = I.decode_inputs(sp, seed=360 + total % 97, lengths=[4 * k + 400, 2 * k])
+    rng = np.random.default_rng(361 + total)
+    nv = np.array([O.n_visible(int(inp["q_pos"][b, 0]), sp.m, int(inp["n_entries"][b]))
+                   for b in range(sp.B)])
+    idx = I.random_index_sets(rng, nv, k, holes=0.05)
+    g = G.upload_decode(inp, d)
+    G.decode_attend(g, idx=torch.from_numpy(idx).reshape(sp.B, 1, k).to(d))
+    torch.cuda.synchronize()
+    out = np64(g.out)
+    for b in range(sp.B):
+        want = OP.decode_attend(inp, b, idx[b])
+        err = np.abs(out[b, 0] - want).max()
+        report("attend split tiles", total=total, b=b, max_abs=err)
+        assert err <= 2e-2
+
+
+@pytest.mark.parametrize("k", [8, 40, 72, 104, 136, 168, 200, 232])
+def test_attend_fp8_unsplit_tile_counts_vs_oracle(k):
+    """FP8 rows with unsplit lists of 1 to 8 tiles (k + 16 window slots): the
+    single-block kernel's loader ring from its shortest lists up."""
+    d = dev()
+    sp = I.CONFIGS["decode_1m_fp4"].replace(B=2, k=k, n_win=16)
+    inp = I.decode_inputs(sp, seed=370 + k, lengths=[4 * k + 100, 300])
+    rng = np.random.default_rng(371 + k)
+    nv = np.array([O.n_visible(int(inp["q_pos"][b, 0]), sp.m, int(inp["n_entries"][b]))
+                   for b in range(sp.B)])
+    idx = I.random_index_sets(rng, nv, k, holes=0.1)
+    g = G.upload_decode(inp, d)
+    G.decode_attend(g, idx=torch.from_numpy(idx).reshape(sp.B, 1, k).to(d))
+    torch.cuda.synchronize()
+    out = np64(g.out)
+    for b in range(sp.B):
+        want = OP.decode_attend(inp, b, idx[b])
+        err = np.abs(out[b, 0] - want).max()
+        report("attend fp8 unsplit tiles", k=k, b=b, max_abs=err)
+        assert err <= 2e-2
+
+
 def test_attend_window_edges_and_empty_selection():
     """Window crossing position 0, all-empty selections (window only), one row."""
     d = dev()
