@@ -174,6 +174,34 @@ def test_indexer_mxfp4_matches_quantized_oracle():
         assert np.all(err <= mx_score_bound(inp, b, ref, nv) + 1e-30)
 
 
+@pytest.mark.parametrize("name", ["decode_64k", "decode_1m_fp4"])
+def test_indexer_decode_step_boundaries(name):
+    """Visible counts on both sides of the decode kernel's step boundaries (bf16
+    steps of 128 entries per block of 4 waves, MXFP4 256; whole triples of steps,
+    then a last one or two): every row is scored to the oracle's bound and the
+    entries past its count stay untouched."""
+    d = dev()
+    nvs = [1, 15, 16, 17, 127, 128, 129, 255, 256, 257, 383, 384, 385, 511, 512, 640, 767,
+           768, 769, 1023, 1024, 1025, 1537, 2049]
+    inp = _decode_small(name, len(nvs), [4 * n for n in nvs], 202)
+    g = G.upload_decode(inp, d)
+    g.scores.fill_(float("nan"))
+    G.decode_indexer(g)
+    torch.cuda.synchronize()
+    S = np64(g.scores)
+    for b, n in enumerate(nvs):
+        ref, nv = OP.decode_scores(inp, b)
+        assert nv == n
+        err = np.abs(S[b, 0, :nv] - ref)
+        if name == "decode_64k":
+            bound = score_error_bound(inp["qI"][b, 0], inp["w"][b, 0], inp["kI"][b], nv)
+        else:
+            bound = mx_score_bound(inp, b, ref, nv)
+        assert np.all(err <= bound + 1e-30), (name, nv)
+        assert np.all(np.isnan(S[b, 0, nv:])), (name, nv)   # invisible entries untouched
+    report("indexer step boundaries", cfg=name, rows=len(nvs))
+
+
 @pytest.mark.parametrize("Tq,offset", [(1031, 0), (37, 4093), (9, 4093)])
 def test_indexer_bf16_query_rows(Tq, offset):
     """Many query rows per sequence (the prefill kernel: a block of rows shares
