@@ -197,7 +197,14 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
   uint32_t key[16];
   const int s0 = tid * 16;
   if (vec) {
-    load_keys16<BF16>(srow, s0, nv, Nmax, key);
+    // a wave whose 1,024 entries all lie past the visible count loads nothing
+    // (its keys are masked everywhere); in a causal prefill that is about half
+    if (__builtin_amdgcn_readfirstlane(tid >> 6) * 1024 < nv) {
+      load_keys16<BF16>(srow, s0, nv, Nmax, key);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) key[i] = 0u;
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
