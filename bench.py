@@ -40,9 +40,9 @@ METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP
 # of known size (--copy-probe).  An entry holds for the kernel source it was
 # taken on (sha256 of the .hip file); after any change it reports null.
 TRAFFIC = {
-    'decode_64k': {"src": "indexer.hip", "sha256": "ad2d5110753ffb440b8c006ac68c3c42619a8ce4beb523e3f3bef522082998ea", "fetch_kib": 67693.5, "write_kib": 2048.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'decode_64k': {"src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 67722.4, "write_kib": 2048.0, "fetch_scale": 1.9998, "write_scale": 1.0},
     'hca_decode_1m': {"src": "attend.hip", "sha256": "ae43da131e40bab8930d9ee5ceba58df2972325b9233c721d116c4efef778fcf", "fetch_kib": 75822.0, "write_kib": 17536.0, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'decode_1m_fp4': {"src": "indexer.hip", "sha256": "ad2d5110753ffb440b8c006ac68c3c42619a8ce4beb523e3f3bef522082998ea", "fetch_kib": 69887.7, "write_kib": 4096.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'decode_1m_fp4': {"src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 69941.2, "write_kib": 4096.0, "fetch_scale": 1.9998, "write_scale": 1.0},
     'prefill_32k': {"src": "attend.hip", "sha256": "ae43da131e40bab8930d9ee5ceba58df2972325b9233c721d116c4efef778fcf", "fetch_kib": 3574817.2, "write_kib": 2097152.9, "fetch_scale": 1.9998, "write_scale": 1.0},
     'prefill_32k_mxfp4': {"src": "attend.hip", "sha256": "ae43da131e40bab8930d9ee5ceba58df2972325b9233c721d116c4efef778fcf", "fetch_kib": 3405804.8, "write_kib": 2097155.9, "fetch_scale": 1.9998, "write_scale": 1.0},
     'oproj_decode': {"src": "oproj.hip", "sha256": "99d8386e33f20e6b4550c52e1cad5985505842be7148f54ce0c4b5e890c9f760", "fetch_kib": 80948.4, "write_kib": 8967.4, "fetch_scale": 1.9998, "write_scale": 1.0},

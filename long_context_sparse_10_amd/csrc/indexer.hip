@@ -544,11 +544,12 @@ hipError_t launch_indexer(const void* qI, const uint8_t* qI_scale, csa_dtype in_
     // covers a multiple of 512 entries (MXFP4) or 128 (bf16), whole steps of
     // its 4 waves (bf16 128 entries, MXFP4 256)
     const int step = in_t == CSA_MXFP4 ? 512 : 128;
-    // MXFP4 keys carry more VALU work per byte (the epilogue outweighs the
-    // matrix core): four waves per SIMD (128 VGPRs) and about four blocks per
-    // CU hide it better than two
-    const int64_t want = in_t == CSA_MXFP4 ? ((int64_t)Nmax * rows + 1023) / 1024
-                                           : ((int64_t)Nmax * rows + 511) / 512;
+    // Blocks per CU, measured: bf16 keys about one (each wave streams a long
+    // range through its ring; decode_64k 28.7 us against 30.1 at two blocks
+    // and 32.2 at four), MXFP4 keys (four waves per SIMD at 128 VGPRs: more
+    // VALU work per byte) about two (30.5 us against 30.8 at four, 32.5 at one)
+    const int64_t want = in_t == CSA_MXFP4 ? ((int64_t)Nmax * rows + 511) / 512
+                                           : ((int64_t)Nmax * rows + 255) / 256;
     int epb = (int)(((want + step - 1) / step) * step);
     epb = epb < 2 * step ? 2 * step : (epb > 8192 ? 8192 : epb);
     dim3 grid((unsigned)(((int64_t)Nmax + epb - 1) / epb * rows));
