@@ -22,8 +22,13 @@ synthetic inputs stand in):
 * decode_1m_fp4 -- 8 sequences x 1,048,576 tokens (262,144 entries), 128
   heads, MXFP4 index keys and queries, FP8/BF16 KV, top-k 1024.
 
-Query-side inputs (q, q^I, w) are drawn directly from N(0, 1): their
-projections sit upstream of the path.  Raw KV / window / index-key values are
+Query-side inputs of the large workloads (q, q^I, w) are drawn directly from
+N(0, 1): their projections sit upstream of the path.  The tiny workloads derive
+them from the hidden states instead, through a rank-64 query latent
+c^Q = h W^DQ (Evidence Ledger Section 2.3.1: the indexer queries come from the
+same compressed query latent as the attention queries): q = c^Q W^UQ,
+q^I = c^Q W^IUQ and w = h W^w, with weights ~ N(0, 1/fan_in), products in fp64
+rounded once to fp32.  Raw KV / window / index-key values are
 drawn N(0, 1) in fp32; normalisation, RoPE and format encoding are done by
 each side itself.  Arrays tagged bf16 are fp32 arrays holding bf16 values
 (rounded with torch's RNE cast).
@@ -59,6 +64,7 @@ class Spec:
     cI: int = 0
     k: int = 0
     dtype: str = "bf16"       # activations / weights / q
+    latent_rank: int = 0      # > 0: q, q^I, w derived from h through a query latent of this rank
     kv_format: str = "bf16"   # "f32", "bf16", "fp8mix"
     index_format: str = "bf16"  # "f32", "bf16", "mxfp4"
     seed: int = 0
@@ -73,9 +79,10 @@ class Spec:
 
 CONFIGS = {
     "tiny_csa": Spec("tiny_csa", "prefill", m=4, c=64, d_r=16, nh=8, T=1024, d=256, nI=4, cI=32,
-                     k=32, dtype="f32", kv_format="f32", index_format="f32", seed=1001),
+                     k=32, dtype="f32", kv_format="f32", index_format="f32", seed=1001,
+                     latent_rank=64),
     "tiny_hca": Spec("tiny_hca", "prefill", m=128, c=64, d_r=16, nh=8, T=1024, d=256,
-                     dtype="f32", kv_format="f32", seed=1001),
+                     dtype="f32", kv_format="f32", seed=1001, latent_rank=64),
     "decode_64k": Spec("decode_64k", "decode", m=4, c=512, d_r=64, nh=64, B=32, L=65536, nI=64,
                        cI=128, k=1024, seed=1002),
     "prefill_32k": Spec("prefill_32k", "prefill", m=4, c=512, d_r=64, nh=64, T=32768, d=4096,
@@ -111,12 +118,14 @@ def cast(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
-def decode_inputs(spec: Spec, seed: Optional[int] = None, lengths=None):
+def decode_inputs(spec: Spec, seed: Optional[int] = None, lengths=None, win_len=None):
     """One decode step for ``spec.B`` sequences.
 
     ``lengths`` (per-sequence context lengths) defaults to ``spec.L`` for all.
     Returns a dict of numpy arrays; the query of sequence b sits at position
     lengths[b] - 1 and the cache holds n_entries[b] = lengths[b] // m entries.
+    The window ring has ``win_len`` slots (default n_win): slot s holds the
+    newest position p <= L-1 with p % win_len == s (-1 while empty).
     """
     rng = np.random.default_rng(spec.seed if seed is None else seed)
     B, c, m = spec.B, spec.c, spec.m
@@ -126,8 +135,8 @@ def decode_inputs(spec: Spec, seed: Optional[int] = None, lengths=None):
     out = dict(spec=spec, lengths=lengths, n_entries=n_entries, Nmax=Nmax,
                q_pos=(lengths - 1).astype(np.int32).reshape(B, 1))
     out["kv_raw"] = _normal(rng, (B, Nmax, c))
-    # window ring: slot s holds the newest position p <= L-1 with p % n_win == s
-    nw = spec.n_win
+    # window ring: slot s holds the newest position p <= L-1 with p % win_len == s
+    nw = spec.n_win if win_len is None else int(win_len)
     win_raw = _normal(rng, (B, nw, c))
     win_pos = np.full((B, nw), -1, dtype=np.int32)
     for b in range(B):
@@ -172,11 +181,35 @@ def prefill_inputs(spec: Spec, seed: Optional[int] = None, T: Optional[int] = No
         out["biasI_a"] = _normal(rng, (m, spec.cI), 0.1)
         out["biasI_b"] = _normal(rng, (m, spec.cI), 0.1)
     out["sink"] = _normal(rng, (spec.nh,))
-    # query side, drawn row by row in blocks so a subset is cheap and identical
     rows = np.arange(T) if queries is None else np.asarray(queries)
     out["q_pos"] = rows.astype(np.int32)
+    if spec.latent_rank:
+        out["q"], out["qI"], out["w"] = _latent_query_rows(rng, out, spec, rows)
+        return out
+    # query side, drawn row by row in blocks so a subset is cheap and identical
     out["q"], out["qI"], out["w"] = _query_rows(spec.seed if seed is None else seed, spec, T, rows)
     return out
+
+
+def _latent_query_rows(rng, out, spec: Spec, rows: np.ndarray):
+    """Query-side inputs from the hidden states through a rank-r query latent
+    (the weights are drawn after every other array, which they leave unchanged):
+    c^Q = h W^DQ, q = c^Q W^UQ, q^I = c^Q W^IUQ, w = h W^w; fp64, then fp32."""
+    d, r = spec.d, spec.latent_rank
+    out["W_DQ"] = _normal(rng, (d, r), 1.0 / d)
+    out["W_UQ"] = _normal(rng, (r, spec.nh * spec.c), 1.0 / r)
+    if spec.nI:
+        out["W_IUQ"] = _normal(rng, (r, spec.nI * spec.cI), 1.0 / r)
+        out["W_w"] = _normal(rng, (d, spec.nI), 1.0 / d)
+    h = np.asarray(out["H"], np.float64)[rows]
+    cq = h @ np.asarray(out["W_DQ"], np.float64)
+    q = (cq @ np.asarray(out["W_UQ"], np.float64)).reshape(len(rows), spec.nh, spec.c)
+    qI = w = None
+    if spec.nI:
+        qI = (cq @ np.asarray(out["W_IUQ"], np.float64)).reshape(len(rows), spec.nI, spec.cI)
+        w = h @ np.asarray(out["W_w"], np.float64)
+        qI, w = cast(qI, spec.dtype), cast(w, "f32")
+    return cast(q, spec.dtype), qI, w
 
 
 _QBLOCK = 256

@@ -137,6 +137,7 @@ class Decode:
     ws_topk: Optional[torch.Tensor] = None
     extra: dict = field(default_factory=dict)
     pool: Optional[PagePool] = None    # set: the caches live in pages (kv / kI / kI_scale unused)
+    win_len: int = 0                   # slots of the window ring (n_win or more)
 
 
 def upload_decode(inp: dict, device="cuda", stream=None) -> Decode:
@@ -153,13 +154,14 @@ def upload_decode(inp: dict, device="cuda", stream=None) -> Decode:
     del raw
     wraw = torch.from_numpy(inp["win_raw"]).to(device)
     wpos = torch.from_numpy(inp["win_pos"].reshape(-1)).to(device)
-    win, _ = encode_rows(wraw, kv_fmt, B * sp.n_win, c, norm_w=gamma, d_r=d_r, pos=wpos,
+    win_len = int(inp["win_raw"].shape[1])
+    win, _ = encode_rows(wraw, kv_fmt, B * win_len, c, norm_w=gamma, d_r=d_r, pos=wpos,
                          stream=stream)
     d = Decode(spec=sp, B=B, Nmax=Nmax, q=to_dev(inp["q"], sp.dtype, device),
                q_pos=torch.from_numpy(inp["q_pos"]).to(device),
                n_entries=torch.from_numpy(inp["n_entries"]).to(device),
                sink=torch.from_numpy(inp["sink"]).to(device), gamma=gamma, kv=kv, win=win,
-               kv_fmt=kv_fmt)
+               kv_fmt=kv_fmt, win_len=win_len)
     d.out = torch.empty(B, 1, sp.nh, c, dtype=torch.bfloat16, device=device)
     if sp.kind == "decode":
         d.index_fmt = FMT[sp.index_format]
@@ -242,12 +244,12 @@ def decode_attend(d: Decode, idx=None, stream=None):
         kv, pages = d.pool.base(_kv_series(d)), d.pool.pages(_kv_series(d))
     if sp.kind == "hca_decode":
         d.ws = C.hca_attend(d.q, qt, d.gamma, EPS, sp.d_r, ROPE_THETA, d.q_pos, kv, d.kv_fmt,
-                            d.Nmax, d.n_entries, sp.m, d.win, sp.n_win, sp.n_win, d.sink, scale,
+                            d.Nmax, d.n_entries, sp.m, d.win, d.win_len, sp.n_win, d.sink, scale,
                             d.B, 1, sp.nh, sp.c, d.out, C.BF16, d.ws, stream, pages=pages)
     else:
         d.ws = C.sparse_mqa_attend(d.q, qt, d.gamma, EPS, sp.d_r, ROPE_THETA, d.q_pos, kv,
                                    d.kv_fmt, d.Nmax, d.idx if idx is None else idx, sp.k, d.win,
-                                   sp.n_win, sp.n_win, d.sink, scale, d.B, 1, sp.nh, sp.c, d.out,
+                                   d.win_len, sp.n_win, d.sink, scale, d.B, 1, sp.nh, sp.c, d.out,
                                    C.BF16, d.ws, stream, pages=pages)
 
 

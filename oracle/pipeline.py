@@ -45,6 +45,9 @@ def decode_cache(inp, b, rows=None):
 
 
 def decode_window(inp, b):
+    """The window ring of sequence b as stored: slot s holds the row of the
+    newest position p with p % win_len == s (RMSNorm, RoPE at p), win_len being
+    the ring's length (at least n_win)."""
     sp = inp["spec"]
     pos = inp["win_pos"][b]
     E = O.rope(O.rms_norm(inp["win_raw"][b], None, EPS), np.maximum(pos, 0), sp.d_r, THETA)
@@ -78,7 +81,8 @@ def decode_attend(inp, b, idx):
     else:
         sel = np.asarray([s for s in idx if s >= 0], dtype=np.int64)
     kv_rows = decode_cache(inp, b, sel) if sel.size else np.zeros((0, sp.c))
-    X = np.concatenate([kv_rows, win[O.window_positions(p, sp.n_win) % sp.n_win]], axis=0)
+    win_len = win.shape[0]                  # the ring's own length, n_win or more
+    X = np.concatenate([kv_rows, win[O.window_positions(p, sp.n_win) % win_len]], axis=0)
     return O.attend_query(inp["q"][b, 0], None, EPS, sp.d_r, THETA, p, X, inp["sink"], tau)
 
 

@@ -66,3 +66,70 @@ def mx_score_bound(inp, b, ref, nv):
 
 def report(name, **kv):
     print(f"[parity] {name}: " + ", ".join(f"{k}={v}" for k, v in kv.items()), flush=True)
+
+
+# ---------------------------------------------------------------- attention checks
+def _row_bytes(fmt, c, d_r):
+    return {L.F32: 4 * c, L.BF16: 2 * c, L.FP8MIX: (c - d_r) + 2 * d_r}[fmt]
+
+
+def kernel_rows(kv, win, fmt, c, d_r, rows_per_seq, win_len, b, sel, pos, n_win):
+    """The rows one query reads, decoded from the GPU's own stored bytes (so a
+    check against them isolates the attention arithmetic): compressed entries
+    ``sel`` of sequence b of a [B, rows_per_seq] cache, then the window ring's
+    positions max(0, pos-n_win+1)..pos at slots p % win_len."""
+    rb = _row_bytes(fmt, c, d_r)
+    kvb = kv.reshape(-1).view(torch.uint8).reshape(-1, rows_per_seq, rb)
+    winb = win.reshape(-1).view(torch.uint8).reshape(-1, win_len, rb)
+    sel = np.asarray(sel, np.int64)
+    parts = []
+    if sel.size:
+        g = kvb[b, torch.from_numpy(sel).to(kvb.device)].contiguous()
+        parts.append(decode_rows(g, fmt, sel.size, c, d_r))
+    wp = np.arange(max(0, pos - n_win + 1), pos + 1)
+    if wp.size:
+        g = winb[b, torch.from_numpy(wp % win_len).to(winb.device)].contiguous()
+        parts.append(decode_rows(g, fmt, wp.size, c, d_r))
+    return np.concatenate(parts, 0) if parts else np.zeros((0, c))
+
+
+def check_attention(tag, got, q_raw, X, sink, tau, d_r, pos, sel_slots, kslots, n_win,
+                    oracle_out, Tq=1, bar=2e-2, **kv):
+    """Two checks of one query row's output [nh, c]: the acceptance bar against
+    the oracle (its own caches and query), and the per-element bound of the
+    kernels' arithmetic against the reference built on the same stored rows X
+    (kernel slot order) and the kernel's bf16 query operand."""
+    from tests.attn_bound import attend_ref_bound, slot_splits
+    got = np.asarray(got, np.float64)
+    sid = slot_splits(sel_slots, kslots, n_win, pos, Tq)
+    ref, bound = attend_ref_bound(q_raw, X, sink, tau, d_r, pos, sid)
+    over = np.abs(got - ref) - bound
+    err = float(np.abs(got - oracle_out).max())
+    ratio = float((np.abs(got - ref) / bound).max())
+    report(tag, max_abs=err, bound_ratio=round(ratio, 3), **kv)
+    assert err <= bar, (tag, err)
+    assert np.all(over <= 0), (tag, float(over.max()), np.unravel_index(int(np.argmax(over)), over.shape))
+    return err
+
+
+def check_decode_attention(tag, g, inp, b, idx_row, out_row, **kv):
+    """check_attention for sequence b of an uploaded decode batch ``g``
+    (pipeline.Decode with dense caches): CSA over ``idx_row``, or HCA over
+    every visible entry when the workload is HCA."""
+    import math
+    from oracle import csa as O
+    from oracle import pipeline as OP
+    sp = inp["spec"]
+    p = int(inp["q_pos"][b, 0])
+    if sp.kind == "hca_decode":
+        nv = int(O.n_visible(p, sp.m, int(inp["n_entries"][b])))
+        sel_slots, sel, kslots = list(range(nv)), np.arange(nv), g.Nmax
+        want = OP.decode_attend(inp, b, None)
+    else:
+        idx_row = np.asarray(idx_row)
+        sel_slots = [v for v, s in enumerate(idx_row) if s >= 0]
+        sel, kslots = idx_row[sel_slots], len(idx_row)
+        want = OP.decode_attend(inp, b, idx_row)
+    X = kernel_rows(g.kv, g.win, g.kv_fmt, sp.c, sp.d_r, g.Nmax, g.win_len, b, sel, p, sp.n_win)
+    return check_attention(tag, out_row, inp["q"][b, 0], X, inp["sink"], 1 / math.sqrt(sp.c),
+                           sp.d_r, p, sel_slots, kslots, sp.n_win, want, **kv)

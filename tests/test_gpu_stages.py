@@ -14,8 +14,8 @@ from long_context_sparse_10_amd import pipeline as G
 from oracle import csa as O
 from oracle import formats as F
 from oracle import pipeline as OP
-from tests.gpu_util import (bf16_ulp, decode_rows, mx_score_bound, dev, e4m3_ulp, np64, report,
-                            score_error_bound)
+from tests.gpu_util import (bf16_ulp, check_decode_attention, decode_rows, dev, e4m3_ulp,
+                            mx_score_bound, np64, report, score_error_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -400,10 +400,8 @@ def test_attend_decode_vs_oracle(name, lengths):
     torch.cuda.synchronize()
     out = np64(g.out)
     for b in range(sp.B):
-        want = OP.decode_attend(inp, b, idx[b] if idx is not None else None)
-        err = np.abs(out[b, 0] - want).max()
-        report("attend", cfg=name, b=b, max_abs=err)
-        assert err <= 2e-2
+        check_decode_attention("attend", g, inp, b, idx[b] if idx is not None else None, out[b, 0],
+                               cfg=name, b=b)
 
 
 @pytest.mark.parametrize("k,lengths,holes,qf32", [
@@ -433,10 +431,7 @@ def test_attend_unsplit_rows_vs_oracle(k, lengths, holes, qf32):
     torch.cuda.synchronize()
     out = np64(g.out)
     for b in range(sp.B):
-        want = OP.decode_attend(inp, b, idx[b])
-        err = np.abs(out[b, 0] - want).max()
-        report("attend unsplit", k=k, b=b, max_abs=err)
-        assert err <= 2e-2
+        check_decode_attention("attend unsplit", g, inp, b, idx[b], out[b, 0], k=k, b=b)
 
 
 @pytest.mark.parametrize("total", [900, 950, 980, 1000, 1100, 1300, 1700, 2000, 2300, 2700, 3000])
@@ -459,10 +454,7 @@ def test_attend_split_tile_counts_vs_oracle(total):
     torch.cuda.synchronize()
     out = np64(g.out)
     for b in range(sp.B):
-        want = OP.decode_attend(inp, b, idx[b])
-        err = np.abs(out[b, 0] - want).max()
-        report("attend split tiles", total=total, b=b, max_abs=err)
-        assert err <= 2e-2
+        check_decode_attention("attend split tiles", g, inp, b, idx[b], out[b, 0], total=total, b=b)
 
 
 @pytest.mark.parametrize("k", [8, 40, 72, 104, 136, 168, 200, 232])
@@ -481,10 +473,7 @@ def test_attend_fp8_unsplit_tile_counts_vs_oracle(k):
     torch.cuda.synchronize()
     out = np64(g.out)
     for b in range(sp.B):
-        want = OP.decode_attend(inp, b, idx[b])
-        err = np.abs(out[b, 0] - want).max()
-        report("attend fp8 unsplit tiles", k=k, b=b, max_abs=err)
-        assert err <= 2e-2
+        check_decode_attention("attend fp8 unsplit tiles", g, inp, b, idx[b], out[b, 0], k=k, b=b)
 
 
 def test_attend_window_edges_and_empty_selection():
@@ -498,8 +487,7 @@ def test_attend_window_edges_and_empty_selection():
     torch.cuda.synchronize()
     out = np64(g.out)
     for b in range(sp.B):
-        want = OP.decode_attend(inp, b, idx[b])
-        assert np.abs(out[b, 0] - want).max() <= 2e-2
+        check_decode_attention("attend window edges", g, inp, b, idx[b], out[b, 0], b=b)
 
 
 def test_attend_deterministic_and_batch_invariant():
