@@ -112,7 +112,7 @@ def check_attention(tag, got, q_raw, X, sink, tau, d_r, pos, sel_slots, kslots, 
     return err
 
 
-def check_decode_attention(tag, g, inp, b, idx_row, out_row, **kv):
+def check_decode_attention(tag, g, inp, seq, idx_row, out_row, **kv):
     """check_attention for sequence b of an uploaded decode batch ``g``
     (pipeline.Decode with dense caches): CSA over ``idx_row``, or HCA over
     every visible entry when the workload is HCA."""
@@ -120,6 +120,7 @@ def check_decode_attention(tag, g, inp, b, idx_row, out_row, **kv):
     from oracle import csa as O
     from oracle import pipeline as OP
     sp = inp["spec"]
+    b = seq
     p = int(inp["q_pos"][b, 0])
     if sp.kind == "hca_decode":
         nv = int(O.n_visible(p, sp.m, int(inp["n_entries"][b])))
