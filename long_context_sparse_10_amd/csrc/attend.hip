@@ -40,6 +40,18 @@ __device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// acc + the sum of squares of 8 packed bf16 values (v_dot2_f32_bf16 per pair).
+// The words are taken as named components: indexing the vector inside an
+// unrolled loop made the compiler square word 0 four times.
+__device__ __forceinline__ float sumsq_bf16x8(u32x4 w, float acc) {
+  const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), __builtin_bit_cast(bf16x2_t, w0), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), __builtin_bit_cast(bf16x2_t, w1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2), __builtin_bit_cast(bf16x2_t, w2), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w3), __builtin_bit_cast(bf16x2_t, w3), acc, false);
+  return acc;
+}
 // two fp32 -> packed bf16 (round to nearest even) by v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
@@ -223,12 +235,12 @@ __device__ __forceinline__ int xrow(int e) {
 }
 
 struct AttendSmem {
-  uint16_t Q[64][AT_LDX];           // normalised, RoPE'd queries of the block's 64 heads
+  uint16_t Q[64][AT_LDX];           // prepared queries of the block's 64 heads (bf16)
   uint16_t X[2][AT_TILE][AT_LDX];   // gathered rows (double-buffered tiles), rows permuted by xrow
   int32_t slot[AT_TAB + 64];
   uint32_t vmask[AT_TAB / 32 + 2];
   float rcs[AT_C / 2][2];           // cos / sin of the query position for each RoPE pair
-  float qg[AT_C];                   // query RMSNorm gains
+  f32x4 qc[AT_C / 2];               // query coefficients per channel pair (see attend_mfma_kernel)
 };
 
 // load 8 consecutive elements (dims d..d+7) of a q row as fp32
@@ -319,7 +331,7 @@ __device__ __forceinline__ void attend_store_out(const AttendArgs& a, int row, i
       *reinterpret_cast<f32x4*>(orow + 4 * d0) = f32x4{v[0], v[1], v[2], v[3]};
     } else {
       *reinterpret_cast<uint2*>(orow + 2 * d0) =
-          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          make_uint2(pack_bf16x2_hw(v[0], v[1]), pack_bf16x2_hw(v[2], v[3]));
     }
   }
 }
@@ -456,27 +468,28 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   const int ntiles = v1 > v0 ? (v1 - v0 + AT_TILE - 1) / AT_TILE : 0;
   const int64_t rb = ctx.rb;
 
-  // ---- raw query rows, loads issued first so they overlap the table pass:
-  // wave w prepares heads 8w..8w+7 of the block, 8 lanes per head, lane part p
-  // holding dims 64j + 8p .. +7 (j = 0..7)
-  const int qhl = 8 * wave + (lane >> 3), qp8 = 8 * (lane & 7);
-  const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)row * a.nh + 64 * hg + qhl) * row_bytes(a.q_t, AT_C, 0);
-  u32x4 qraw[8];
-  if (a.q_t == CSA_BF16) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qraw[j] = *reinterpret_cast<const u32x4*>(qrow + 2 * (64 * j + qp8));
-  }
+  // the query row of a math lane: lane (g, li) takes dims 128g .. 128g+127 of
+  // head `head`, the layout of the S^T operand
+  const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)row * a.nh + head) * row_bytes(a.q_t, AT_C, 0);
 
-  // ---- RoPE angles of the query position, one pair per thread (shared by all
-  // heads; the output's inverse rotation reuses them with the sine negated)
-  for (int u = tid; u < d_r / 2; u += 512) {
-    float cs, sn;
-    rope_cs(rt, (double)ctx.qp, u, &cs, &sn);
-    sm.rcs[u][0] = cs;
-    sm.rcs[u][1] = sn;
+  // ---- per channel pair p (channels 2p, 2p+1), one per thread: the RoPE
+  // angle of the query position (the output's inverse rotation reuses it with
+  // the sine negated) and the query coefficients, which fold the RMSNorm gains
+  // (g0, g1), the rotation (c, s; 1, 0 outside the RoPE channels) and
+  // tau * log2 e into qc = (g0 c, g1 s, g0 s, g1 c) * tau * log2 e: the
+  // prepared pair is (inv (qc.x x0 - qc.y x1), inv (qc.z x0 + qc.w x1))
+  for (int p = tid; p < AT_C / 2; p += 512) {
+    float cs = 1.f, sn = 0.f;
+    if (2 * p >= AT_C - d_r) {
+      const int u = p - (AT_C - d_r) / 2;
+      rope_cs(rt, (double)ctx.qp, u, &cs, &sn);
+      sm.rcs[u][0] = cs;
+      sm.rcs[u][1] = sn;
+    }
+    const float g0 = a.q_norm_w != nullptr ? a.q_norm_w[2 * p] : 1.f;
+    const float g1 = a.q_norm_w != nullptr ? a.q_norm_w[2 * p + 1] : 1.f;
+    sm.qc[p] = f32x4{g0 * cs * qscale, g1 * sn * qscale, g0 * sn * qscale, g1 * cs * qscale};
   }
-  // ---- query RMSNorm gains (1 without a gain vector)
-  if (tid < AT_C) sm.qg[tid] = a.q_norm_w != nullptr ? a.q_norm_w[tid] : 1.f;
   // ---- slot table and per-tile validity masks (one coalesced pass)
   for (int i = tid; i < ((ntiles * AT_TILE + 63) & ~63); i += 512) {
     const int v = v0 + i;
@@ -490,59 +503,51 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   }
   __syncthreads();  // slot table and RoPE angles ready
 
-  // ---- queries to LDS (B operand of S^T): RMSNorm over the head, RoPE at q
+  // ---- the math wave's queries (B operand of S^T) to LDS: RMSNorm over the
+  // head (its four lane groups), then the coefficient table (gains, RoPE at q,
+  // tau * log2 e), bf16.  Each math lane prepares exactly the fragments it
+  // later reads back as its operand; kept in shared memory, they can be
+  // re-read instead of held through the tile loop.
 #define CSA_QPREP()                                                                          \
   {                                                                                          \
-    float ss = 0.f;                                                                          \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                          \
-      float v[8];                                                                            \
-      if (a.q_t == CSA_BF16) {                                                               \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-          v[2 * i] = __uint_as_float(qraw[j][i] << 16);                                      \
-          v[2 * i + 1] = __uint_as_float(qraw[j][i] & 0xFFFF0000u);                          \
-        }                                                                                    \
-      } else {                                                                               \
-        load8(qrow, a.q_t, 64 * j + qp8, v);                                                 \
-      }                                                                                      \
-      _Pragma("unroll") for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);               \
+    u32x4 qraw[16];                                                                          \
+    if (a.q_t == CSA_BF16) {                                                                 \
+      _Pragma("unroll") for (int ks = 0; ks < 16; ++ks)                                      \
+        qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 2 * (128 * g + 8 * ks));           \
     }                                                                                        \
-    ss += __shfl_xor(ss, 1);                                                                 \
-    ss += __shfl_xor(ss, 2);                                                                 \
-    ss += __shfl_xor(ss, 4);                                                                 \
+    float ssp[4] = {0.f, 0.f, 0.f, 0.f};                                                     \
+    _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                      \
+      if (a.q_t == CSA_BF16) {                                                               \
+        /* sum of squares straight from the packed bf16 pairs (v_dot2) */                    \
+        ssp[ks & 3] = sumsq_bf16x8(qraw[ks], ssp[ks & 3]);                                   \
+      } else {                                                                               \
+        float v[8];                                                                          \
+        load8(qrow, a.q_t, 128 * g + 8 * ks, v);                                             \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i) ssp[ks & 3] = fmaf(v[i], v[i], ssp[ks & 3]); \
+      }                                                                                      \
+    }                                                                                        \
+    float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);                                        \
+    ss += __shfl_xor(ss, 16);                                                                \
+    ss += __shfl_xor(ss, 32);                                                                \
     const float inv = 1.0f / sqrtf(ss / (float)AT_C + a.eps);                                \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                          \
-      const int d0 = 64 * j + qp8;                                                           \
+    _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                      \
       float v[8];                                                                            \
       if (a.q_t == CSA_BF16) {                                                               \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-          v[2 * i] = __uint_as_float(qraw[j][i] << 16);                                      \
-          v[2 * i + 1] = __uint_as_float(qraw[j][i] & 0xFFFF0000u);                          \
+          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);                                     \
+          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);                         \
         }                                                                                    \
       } else {                                                                               \
-        load8(qrow, a.q_t, d0, v);                                                           \
+        load8(qrow, a.q_t, 128 * g + 8 * ks, v);                                             \
       }                                                                                      \
-      {                                                                                      \
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.qg[d0]);                        \
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.qg[d0 + 4]);                    \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-          v[i] *= inv * g0[i];                                                               \
-          v[4 + i] *= inv * g1[i];                                                           \
-        }                                                                                    \
-      }                                                                                      \
-      _Pragma("unroll") for (int i = 0; i < 8; i += 2) {                                     \
-        const int d = d0 + i;                                                                \
-        if (d >= AT_C - d_r) {                                                               \
-          const float cs = sm.rcs[(d - (AT_C - d_r)) >> 1][0];                               \
-          const float sn = sm.rcs[(d - (AT_C - d_r)) >> 1][1];                               \
-          const float x0 = v[i], x1 = v[i + 1];                                              \
-          v[i] = x0 * cs - x1 * sn;                                                          \
-          v[i + 1] = x0 * sn + x1 * cs;                                                      \
-        }                                                                                    \
-      }                                                                                      \
+      const f32x4* c4 = &sm.qc[(128 * g + 8 * ks) >> 1];                                     \
       u32x4 pk;                                                                              \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                          \
-        pk[i] = pack_bf16x2_hw(v[2 * i] * qscale, v[2 * i + 1] * qscale);                    \
-      *reinterpret_cast<u32x4*>(&sm.Q[qhl][d0]) = pk;                                        \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                        \
+        const f32x4 c = c4[i];                                                               \
+        const float x0 = v[2 * i] * inv, x1 = v[2 * i + 1] * inv;                            \
+        pk[i] = pack_bf16x2_hw(fmaf(c[0], x0, -c[1] * x1), fmaf(c[2], x0, c[3] * x1));       \
+      }                                                                                      \
+      *reinterpret_cast<u32x4*>(&sm.Q[16 * mw + li][128 * g + 8 * ks]) = pk;                 \
     }                                                                                        \
   }
 
@@ -622,7 +627,6 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
       CSA_STAGE(st0, ok0, 0);
       CSA_STAGE(st1, ok1, 1);
     }
-    CSA_QPREP();
     if (ntiles > 0) {
       CSA_COMMIT(st0, ok0, 0);
       CSA_STAGE(st0, ok0, 2);
@@ -658,12 +662,13 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
 #undef CSA_LAST_PHASE
     return;
   }
+  // this wave's queries: loads and preparation overlap the loaders' first gathers
+  CSA_QPREP();
   float m_run = kNegBig, l_run = 0.f;
   f32x4 O[32];
 #pragma unroll
   for (int nd = 0; nd < 32; ++nd) O[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  CSA_QPREP();
-  __syncthreads();  // queries and tile 0 in LDS
+  __syncthreads();  // tile 0 in LDS
   // this wave's query fragments (B operand of S^T), kept in registers
   bf16x8 qf[16];
 #pragma unroll
@@ -694,7 +699,7 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
 #pragma unroll
     for (int nd = 0; nd < 32; ++nd)
       *reinterpret_cast<uint2*>(wo + 16 * nd + 4 * g) =
-          make_uint2(pack_bf16x2(O[nd][0] * il, O[nd][1] * il), pack_bf16x2(O[nd][2] * il, O[nd][3] * il));
+          make_uint2(pack_bf16x2_hw(O[nd][0] * il, O[nd][1] * il), pack_bf16x2_hw(O[nd][2] * il, O[nd][3] * il));
     if (g == 0) {
       const int64_t nrows = (int64_t)a.B * a.Tq;
       float* wml = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(ws) + nrows * nsplit * a.nh * AT_C) +
