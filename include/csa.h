@@ -292,8 +292,9 @@ csa_status grouped_out_proj(const void* o, csa_dtype t, int R, int nh, int c, in
                             void* ws, size_t* ws_bytes, hipStream_t stream);
 
 /*
- * Paged caches (Evidence Ledger Section 3.5.1; shuhuayu section 06 "Hybrid
- * attention creates a hybrid cache"): compressed entries live in fixed-size
+ * Paged caches (Evidence Ledger Section 3.5.1; "G2C Brief -- DeepSeek V4",
+ * "Hybrid attention creates a hybrid cache"; shuhuayu section 06 "What grows
+ * with context" for the per-entry bytes): compressed entries live in fixed-size
  * blocks covering lcm(m, m') tokens, so one block of 128 tokens holds 32 CSA
  * entries (main rows and index keys) and 1 HCA entry.  A block is a PAGE of a
  * caller-owned pool; the page holds each series in its own section at an

@@ -47,7 +47,8 @@ def encode_rows(x: torch.Tensor, fmt: int, rows: int, c: int, *, norm_w=None, d_
 # ============================================================ paged caches
 @dataclass
 class PagePool:
-    """A hybrid page pool (Evidence Ledger Section 3.5.1; shuhuayu section 06):
+    """A hybrid page pool (Evidence Ledger Section 3.5.1; "G2C Brief -- DeepSeek
+    V4", "Hybrid attention creates a hybrid cache"):
     one page per 128-token block of a sequence, each series of entries in its
     own section of the page.  ``sections[name] = (byte offset, entries_log2,
     row bytes)``; ``table[b, j]`` is the page of block j of sequence b."""

@@ -12,8 +12,8 @@ Formats (all rounding is round-to-nearest, ties-to-even):
   Section 5.2.1).
 * e4m3 -- OCP FP8 "E4M3FN": bias 7, three mantissa bits, no infinities, largest
   finite value 448; values beyond are saturated to +-448 (our reading: the pages
-  give FP8 storage with no scale bytes, 576 B per entry, shuangyu study page,
-  section 06).
+  give FP8 storage with no scale bytes, 576 B per entry: "DeepSeek V4 study"
+  (shuhuayu), section 06 "What grows with context").
 * E2M1 / MXFP4 -- OCP MX FP4 elements {0, 0.5, 1, 1.5, 2, 3, 4, 6} in blocks of
   32 sharing one e8m0 power-of-two scale 2^(floor(log2 amax) - 2) (Evidence
   Ledger page, Section 5.2.1: MXFP4 (E2M1) in 1x32 tiles).  Elements saturate
