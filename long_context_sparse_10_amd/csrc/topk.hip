@@ -13,10 +13,12 @@
 // (the candidates) are compacted into LDS and one wave resolves the remaining
 // digits over them alone (past TK_CAND_CAP candidates the block resolves them
 // over the keys in registers instead); the ordered compaction is a single
-// block-wide scan.  Longer rows (few decode rows over 2^18 entries) spread over
-// many blocks per row: per-block digit histograms, a per-row reduction that
-// fixes the digit, and after the last digit per-block counts and an ordered
-// emit at each block's offset.
+// block-wide scan.  Longer rows spread over many blocks per row: bf16 scores
+// (decode rows of up to 2^24 entries) in two launches -- per-slice 16-bit key
+// histograms kept above each slice's own k-th largest key, then per slice the
+// row's K* and the slice's ordered write -- and fp32 scores by a per-digit
+// sequence of slice histograms and per-row reductions, then per-slice counts
+// and an ordered emit at each slice's offset.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -533,13 +535,415 @@ __global__ __launch_bounds__(TKM_THREADS) void topk_emit_kernel(
   }
 }
 
+// ------------------------------------------------------------------ long bf16 rows
+// Rows of more than 16 * 1024 bf16 scores (decode at 1M context: 2^18 entries
+// per row) in two launches over (row, slice) blocks; no block reads more than
+// its own slice of TKF_SLICE entries.
+//  1. topk_fine_hist_kernel counts the slice's 16-bit keys in an LDS histogram
+//     (two 16-bit counters per word), finds the slice's own k-th largest key lo
+//     (its smallest key when it holds fewer than k) and its largest key hi, and
+//     stores lo, hi, its entry count and the histogram over [lo, hi].  A slice
+//     with k or more entries holds k keys >= its lo, so the row's k-th largest
+//     key K* is at least the largest such lo, L: every key >= L of every slice
+//     lies in that slice's stored range.
+//  2. topk_fine_emit_kernel: each slice block of the row sums the stored
+//     histograms over 1024 keys at a time from the row's largest key down
+//     until the rank k is reached, which fixes K*, the number of keys above it
+//     and -- from the part of the sums over the slices before its own -- the
+//     slice's output offset and the K*-ties already taken; then the slice's keys
+//     above K* and the K*-ties the row still needs, lowest index first, are
+//     written in ascending entry order.
+// Rows run in groups of at most TKF_MAX_SLICES / P (P slices per row) per
+// launch pair, which bounds the workspace: per slice a 16-byte header and a
+// 128 KB histogram addressed by key (only [lo, hi] is written and read).
+constexpr int TKF_THREADS = 1024;
+constexpr int TKF_SLICE = 16 * TKF_THREADS;   // entries per slice block
+constexpr int TKF_KEYS = 1 << 16;             // bf16 keys
+constexpr int TKF_MAX_SLICES = 1024;          // slices per launch pair
+static_assert(TKF_KEYS / 64 == TKF_THREADS, "one 64-key group per thread");
+static_assert(TKF_MAX_SLICES % TKF_THREADS == 0, "whole header rounds");
+
+struct TkfSlice {
+  int lo, hi, count, pad;
+};
+
+static size_t tkf_hdr_bytes(int64_t slices) {
+  return (size_t)((slices * (int64_t)sizeof(TkfSlice) + 255) / 256 * 256);
+}
+
+// Wave-wide helpers on DPP row moves (no LDS round trips); every lane of the
+// wave must be active.  DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] =
+// 0x4E, row_ror:n = 0x120 + n, row_shr:n = 0x110 + n.
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int wave_all_max(int x) {
+  x = max(x, dpp_move<0xB1>(x));
+  x = max(x, dpp_move<0x4E>(x));
+  x = max(x, dpp_move<0x124>(x));
+  x = max(x, dpp_move<0x128>(x));  // every lane holds its row's maximum
+  const int a = max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
+  const int b = max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48));
+  return max(a, b);
+}
+__device__ __forceinline__ int wave_all_min(int x) { return -wave_all_max(-x); }
+// inclusive prefix sum over the lanes of the wave
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += dpp_move<0x111>(x);
+  x += dpp_move<0x112>(x);
+  x += dpp_move<0x114>(x);
+  x += dpp_move<0x118>(x);  // prefix within each row of 16 lanes
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int lane = threadIdx.x & 63;
+  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
+// exclusive scan over the TKF_THREADS threads of a block with one barrier;
+// `ws` (one int per wave) must not be written again before a later barrier
+__device__ __forceinline__ int tkf_block_excl(int v, int* ws, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_sum(v);
+  if (lane == 63) ws[wave] = incl;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < TKF_THREADS / 64; ++i) {
+    const int y = ws[i];
+    pre += i < wave ? y : 0;
+    tot += y;
+  }
+  *total = tot;
+  return incl - v + pre;
+}
+
+// two exclusive scans at once (one barrier); `ws` holds two ints per wave
+__device__ __forceinline__ void tkf_block_excl2(int a, int b, int* ws, int* ex_a, int* ex_b,
+                                                int* tot_a, int* tot_b) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ia = wave_incl_sum(a), ib = wave_incl_sum(b);
+  if (lane == 63) {
+    ws[2 * wave] = ia;
+    ws[2 * wave + 1] = ib;
+  }
+  __syncthreads();
+  int pa = 0, pb = 0, ta = 0, tb = 0;
+#pragma unroll
+  for (int i = 0; i < TKF_THREADS / 64; ++i) {
+    const int ya = ws[2 * i], yb = ws[2 * i + 1];
+    pa += i < wave ? ya : 0;
+    pb += i < wave ? yb : 0;
+    ta += ya;
+    tb += yb;
+  }
+  *ex_a = ia - a + pa;
+  *ex_b = ib - b + pb;
+  *tot_a = ta;
+  *tot_b = tb;
+}
+
+// the raw bf16 scores of entries [s0, s0 + 16) of a row of Nmax (0 past Nmax),
+// as 8 words; tkf_keys turns them into keys where they are first needed, so
+// the loads stay in flight across other requests.  Entries past the row's
+// visible count are masked by the caller.
+__device__ __forceinline__ void tkf_load_raw(const uint16_t* srow, int s0, int Nmax, int vec,
+                                             u32x4* raw) {
+  if (vec && s0 + 16 <= Nmax) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(srow + s0);
+    raw[0] = p[0];
+    raw[1] = p[1];
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = (s0 + 2 * i < Nmax) ? srow[s0 + 2 * i] : 0u;
+      const uint32_t b = (s0 + 2 * i + 1 < Nmax) ? srow[s0 + 2 * i + 1] : 0u;
+      w[i] = a | (b << 16);
+    }
+    raw[0] = u32x4{w[0], w[1], w[2], w[3]};
+    raw[1] = u32x4{w[4], w[5], w[6], w[7]};
+  }
+}
+__device__ __forceinline__ void tkf_keys(const u32x4* raw, uint32_t* key) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      key[8 * j + 2 * i] = bf16_key(raw[j][i] & 0xFFFFu);
+      key[8 * j + 2 * i + 1] = bf16_key(raw[j][i] >> 16);
+    }
+}
+
+// count of key kk in the packed LDS histogram
+__device__ __forceinline__ int tkf_count(const uint32_t* h, int kk) {
+  const uint32_t v = h[kk >> 1];
+  return (int)((kk & 1) ? (v >> 16) : (v & 0xFFFFu));
+}
+// the 64 keys of group g (words 32 g .. 32 g + 31), read from word `rot`
+// mod 32 on so that the lanes of a wave hit distinct banks
+__device__ __forceinline__ int tkf_group_count(const uint32_t* h, int g, int rot) {
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t v = h[32 * g + ((j + rot) & 31)];
+    cnt += (int)(v & 0xFFFFu) + (int)(v >> 16);
+  }
+  return cnt;
+}
+
+__global__ __launch_bounds__(TKF_THREADS) void topk_fine_hist_kernel(
+    const uint16_t* __restrict__ scores, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int row0, int Tq, int Nmax, int m, int k, int vec,
+    int P, TkfSlice* __restrict__ hdr, uint16_t* __restrict__ hist) {
+  // counters of keys 2w (low half) and 2w+1 (high half), all cleared
+  __shared__ __align__(16) uint32_t h[TKF_KEYS / 2];
+  __shared__ __align__(16) int red[2][TKF_THREADS / 64];
+  __shared__ __align__(16) int scan_ws[TKF_THREADS / 64];
+  __shared__ int sh_grp[2];  // group holding the k-th largest key, keys above it
+  __shared__ int sh_lo;
+  const int lr = blockIdx.x / P, p = blockIdx.x % P, tid = threadIdx.x, lane = tid & 63;
+  const int row = row0 + lr;
+  // the slice's keys are requested together with the row's visible count, and
+  // the histogram is cleared while they are in flight
+  const int s0 = p * TKF_SLICE + 16 * tid;
+  u32x4 raw[2];
+  tkf_load_raw(scores + (int64_t)row * Nmax, s0, Nmax, vec, raw);
+  const int nv = row_visible(q_pos, n_entries, row, Tq, Nmax, m);
+  if (nv <= k) return;  // the emit kernel pads such rows; nothing here is read
+  const int cs = min(max(nv - p * TKF_SLICE, 0), TKF_SLICE);
+  if (cs == 0) {
+    if (tid == 0) hdr[blockIdx.x] = TkfSlice{1, 0, 0, 0};
+    return;
+  }
+  u32x4* h4 = reinterpret_cast<u32x4*>(h);
+#pragma unroll
+  for (int j = 0; j < TKF_KEYS / 8 / TKF_THREADS; ++j)
+    h4[tid + j * TKF_THREADS] = u32x4{0u, 0u, 0u, 0u};
+  uint32_t key[16];
+  tkf_keys(raw, key);
+  int kmax = -1, kmin = TKF_KEYS;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (s0 + i < nv) {
+      kmax = max(kmax, (int)key[i]);
+      kmin = min(kmin, (int)key[i]);
+    }
+  kmax = wave_all_max(kmax);
+  kmin = wave_all_min(kmin);
+  if (lane == 0) {
+    red[0][tid >> 6] = kmax;
+    red[1][tid >> 6] = kmin;
+  }
+  __syncthreads();  // histogram cleared, wave extremes stored
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (s0 + i < nv) atomicAdd(&h[key[i] >> 1], 1u << ((key[i] & 1u) << 4));
+  const int hi = wave_all_max(red[0][lane & 15]);
+  int lo = wave_all_min(red[1][lane & 15]);
+  const int w_hi = hi >> 1;
+  __syncthreads();  // histogram complete
+  if (cs >= k) {
+    const int g_hi = hi >> 6, g_lo = lo >> 6;
+    if (g_hi - g_lo < 64) {
+      // one wave: lane j counts group g_hi - j, then the keys of the group found
+      if (tid < 64) {
+        const int g = g_hi - lane;
+        const int cnt = g >= g_lo ? tkf_group_count(h, g, lane) : 0;
+        const int incl = wave_incl_sum(cnt);
+        const uint64_t hit = __ballot(incl - cnt < k && incl >= k);
+        const int jg = (int)__builtin_ctzll(hit);
+        const int gs = max(g_hi - jg, 0), above = __builtin_amdgcn_readlane(incl - cnt, jg & 63);
+        const int kk = 64 * gs + 63 - lane;
+        const int c = tkf_count(h, kk);
+        const int incl2 = wave_incl_sum(c) + above;
+        const uint64_t hit2 = __ballot(incl2 - c < k && incl2 >= k);
+        if (lane == 0) sh_lo = 64 * gs + 63 - (int)__builtin_ctzll(hit2);
+      }
+    } else {
+      // thread t counts group g_hi - t (the range spans at most 1024 groups)
+      const int g = g_hi - tid;
+      const int cnt = g >= g_lo ? tkf_group_count(h, g, tid) : 0;
+      if (tid == 0) {
+        sh_grp[0] = g_lo;
+        sh_grp[1] = 0;
+      }
+      int total;
+      const int excl = tkf_block_excl(cnt, scan_ws, &total);
+      if (excl < k && excl + cnt >= k) {
+        sh_grp[0] = g;
+        sh_grp[1] = excl;
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const int kk = 64 * sh_grp[0] + 63 - lane;
+        const int c = tkf_count(h, kk);
+        const int incl2 = wave_incl_sum(c) + sh_grp[1];
+        const uint64_t hit2 = __ballot(incl2 - c < k && incl2 >= k);
+        if (lane == 0) sh_lo = 64 * sh_grp[0] + 63 - (int)__builtin_ctzll(hit2);
+      }
+    }
+    __syncthreads();
+    lo = min(max(sh_lo, lo), hi);  // within the slice's keys in any case
+  }
+  if (tid == 0) hdr[blockIdx.x] = TkfSlice{lo, hi, cs, 0};
+  uint32_t* dst = reinterpret_cast<uint32_t*>(hist + (int64_t)blockIdx.x * TKF_KEYS);
+  for (int w = (lo >> 1) + tid; w <= w_hi; w += TKF_THREADS) dst[w] = h[w];
+}
+
+__global__ __launch_bounds__(TKF_THREADS) void topk_fine_emit_kernel(
+    const uint16_t* __restrict__ scores, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int row0, int Tq, int Nmax, int m, int k, int vec,
+    int P, const TkfSlice* __restrict__ hdr, const uint16_t* __restrict__ hist,
+    int32_t* __restrict__ idx) {
+  __shared__ TkfSlice sh[TKF_MAX_SLICES];
+  __shared__ __align__(16) int red[2][TKF_THREADS / 64];
+  __shared__ __align__(16) int ws_cb[2 * (TKF_THREADS / 64)];
+  __shared__ __align__(16) int ws_e[TKF_THREADS / 64];
+  __shared__ int res[4];  // K*, keys above K*, of them in earlier slices, K*-ties in earlier slices
+  const int lr = blockIdx.x / P, p = blockIdx.x % P, tid = threadIdx.x, lane = tid & 63;
+  const int row = row0 + lr;
+  // this slice's keys and the row's slice headers are requested together with
+  // the row's visible count; the keys stay in flight while K* is found
+  const int slice0 = p * TKF_SLICE;
+  const int s0 = slice0 + 16 * tid;
+  u32x4 raw[2];
+  tkf_load_raw(scores + (int64_t)row * Nmax, s0, Nmax, vec, raw);
+  const TkfSlice* hr = hdr + (int64_t)lr * P;
+  TkfSlice hd[TKF_MAX_SLICES / TKF_THREADS];
+#pragma unroll
+  for (int j = 0; j < TKF_MAX_SLICES / TKF_THREADS; ++j) {
+    const int i = tid + j * TKF_THREADS;
+    if (i < P) hd[j] = hr[i];
+  }
+  const int nv = row_visible(q_pos, n_entries, row, Tq, Nmax, m);
+  int32_t* out = idx + (int64_t)row * k;
+  if (nv <= k) {
+    for (int i = p * TKF_THREADS + tid; i < k; i += P * TKF_THREADS) out[i] = i < nv ? i : -1;
+    return;
+  }
+  if (slice0 >= nv) return;
+  const int pv = (nv + TKF_SLICE - 1) / TKF_SLICE;  // slices holding visible entries
+  int L = -1, H = -1;
+#pragma unroll
+  for (int j = 0; j < TKF_MAX_SLICES / TKF_THREADS; ++j) {
+    const int i = tid + j * TKF_THREADS;
+    if (i < pv) {
+      const TkfSlice d = hd[j];
+      sh[i] = d;
+      if (d.count >= k) L = max(L, d.lo);
+      H = max(H, d.hi);
+    }
+  }
+  L = wave_all_max(L);
+  H = wave_all_max(H);
+  if (lane == 0) {
+    red[0][tid >> 6] = L;
+    red[1][tid >> 6] = H;
+  }
+  if (tid < 4) res[tid] = tid == 0 ? -1 : 0;
+  __syncthreads();
+  L = wave_all_max(red[0][lane & 15]);
+  H = wave_all_max(red[1][lane & 15]);
+  // rank k from the top: thread t takes key top - t; counts of all slices (c)
+  // and of the slices before this one (cb)
+  const uint16_t* hrow = hist + (int64_t)lr * P * TKF_KEYS;
+  int carry = 0, carry_before = 0;
+  for (int top = H; top >= L; top -= TKF_THREADS) {
+    const int kx = top - tid;
+    int c = 0, cb = 0;
+    if (kx >= L) {
+      for (int sb = 0; sb < pv; sb += 16) {
+        // unconditional loads from stored bins (slice and key clamped into a
+        // stored range), masked afterwards: all 16 are in flight at once
+        uint32_t v[16];
+        bool in[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int sl = min(sb + j, pv - 1);
+          const int lo = sh[sl].lo, hi = sh[sl].hi;
+          in[j] = sb + j < pv && kx >= lo && kx <= hi;
+          v[j] = hrow[(int64_t)sl * TKF_KEYS + min(max(kx, lo), hi)];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = in[j] ? v[j] : 0u;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          c += (int)v[j];
+          cb += sb + j < p ? (int)v[j] : 0;
+        }
+      }
+    }
+    int ex_c, ex_b, tot_c, tot_b;
+    tkf_block_excl2(c, cb, ws_cb, &ex_c, &ex_b, &tot_c, &tot_b);
+    ex_c += carry;
+    ex_b += carry_before;
+    if (kx >= L && ex_c < k && ex_c + c >= k) {
+      res[0] = kx;
+      res[1] = ex_c;
+      res[2] = ex_b;
+      res[3] = cb;
+    }
+    __syncthreads();
+    if (res[0] >= 0) break;
+    carry += tot_c;
+    carry_before += tot_b;
+  }
+  const uint32_t kstar = (uint32_t)res[0];
+  const int need_eq = k - res[1];
+  // ordered write of this slice's selection at its offset
+  uint32_t key[16];
+  tkf_keys(raw, key);
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool ok = s0 + i < nv;
+    gt += (ok && key[i] > kstar) ? 1 : 0;
+    eq += (ok && key[i] == kstar) ? 1 : 0;
+  }
+  int total;
+  const int excl = tkf_block_excl(gt | (eq << 16), ws_e, &total);
+  int gt_before = res[2] + (excl & 0xFFFF), eq_before = res[3] + (excl >> 16);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool ok = s0 + i < nv;
+    const bool g = ok && key[i] > kstar, e = ok && key[i] == kstar;
+    if (g || (e && eq_before < need_eq)) {
+      const int pos = gt_before + min(eq_before, need_eq);
+      if (pos >= 0 && pos < k) out[pos] = s0 + i;
+    }
+    gt_before += g ? 1 : 0;
+    eq_before += e ? 1 : 0;
+  }
+}
+
+static bool topk_bf16_long(csa_dtype score_t, int Nmax, int k) {
+  return score_t == CSA_BF16 && Nmax > 16 * 1024 && k <= TKF_SLICE &&
+         (Nmax + TKF_SLICE - 1) / TKF_SLICE <= TKF_MAX_SLICES;
+}
+
 static bool topk_multiblock(int Nmax) { return Nmax > 16 * 1024; }
+
+// rows per launch pair of the long bf16 path
+static int tkf_group(int64_t rows, int P) {
+  const int64_t g = TKF_MAX_SLICES / P;
+  return (int)(rows < g ? rows : g);
+}
 
 size_t topk_workspace(int B, int Tq, int Nmax) {
   if (!topk_multiblock(Nmax)) return 0;
   const int64_t rows = (int64_t)B * Tq;
   const int64_t P = (Nmax + TKM_SLICE - 1) / TKM_SLICE;
-  return (size_t)(rows * 4 + rows * P * 2048 + rows * P * 2) * sizeof(int);
+  // the larger of the two long-row paths (per-digit slice histograms and
+  // counts; bf16 keys: per-slice 16-bit histograms of one row group)
+  const size_t multi = (size_t)(rows * 4 + rows * P * 2048 + rows * P * 2) * sizeof(int);
+  const int64_t Pf = (Nmax + TKF_SLICE - 1) / TKF_SLICE;
+  size_t fine = 0;
+  if (Pf <= TKF_MAX_SLICES && rows > 0) {
+    const int64_t slices = (int64_t)tkf_group(rows, (int)Pf) * Pf;
+    fine = tkf_hdr_bytes(slices) + (size_t)slices * TKF_KEYS * sizeof(uint16_t);
+  }
+  return multi > fine ? multi : fine;
 }
 
 hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_pos,
@@ -550,6 +954,22 @@ hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_p
   const bool bf = score_t == CSA_BF16;
   // whole 16-byte key loads need 16-byte aligned rows
   const int vec = ((uintptr_t)scores % 16 == 0) && (bf ? Nmax % 8 == 0 : Nmax % 4 == 0);
+  if (topk_bf16_long(score_t, Nmax, k)) {
+    const int P = (Nmax + TKF_SLICE - 1) / TKF_SLICE;
+    const int G = tkf_group(rows, P);
+    TkfSlice* hdr = reinterpret_cast<TkfSlice*>(ws);
+    uint16_t* hist = reinterpret_cast<uint16_t*>((char*)ws + tkf_hdr_bytes((int64_t)G * P));
+    for (int r0 = 0; r0 < rows; r0 += G) {
+      const int g = rows - r0 < G ? rows - r0 : G;
+      const dim3 grid((unsigned)(g * P)), t(TKF_THREADS);
+      hipLaunchKernelGGL(topk_fine_hist_kernel, grid, t, 0, s, (const uint16_t*)scores, q_pos,
+                         n_entries, r0, Tq, Nmax, m, k, vec, P, hdr, hist);
+      hipLaunchKernelGGL(topk_fine_emit_kernel, grid, t, 0, s, (const uint16_t*)scores, q_pos,
+                         n_entries, r0, Tq, Nmax, m, k, vec, P, (const TkfSlice*)hdr,
+                         (const uint16_t*)hist, idx);
+    }
+    return hipGetLastError();
+  }
   if (topk_multiblock(Nmax)) {
     const int P = (Nmax + TKM_SLICE - 1) / TKM_SLICE;
     TkRow* st = reinterpret_cast<TkRow*>(ws);

@@ -317,10 +317,16 @@ def _score_rows(rng, kind, rows, N):
         return I.cast(rng.standard_normal((rows, N)).astype(np.float32) * 0.5, "bf16")
     if kind == "bf16ties":  # integers, exact in bf16: equal keys across many slices
         return rng.integers(-40, 41, size=(rows, N)).astype(np.float32)
+    if kind == "bf16ties5":  # tens of thousands of equal keys in one row
+        return rng.integers(-2, 3, size=(rows, N)).astype(np.float32)
+    if kind == "bf16wide":  # magnitudes 2^-120 .. 2^120, both signs: thousands of distinct keys
+        mag = np.exp2(rng.uniform(-120, 120, size=(rows, N)))
+        return I.cast((np.where(rng.random((rows, N)) < 0.5, -mag, mag)).astype(np.float32), "bf16")
     return rng.standard_normal((rows, N)).astype(np.float32)
 
 
-@pytest.mark.parametrize("kind", ["ties", "ties81", "ties5", "bf16", "bf16ties", "normal"])
+@pytest.mark.parametrize("kind", ["ties", "ties81", "ties5", "bf16", "bf16ties", "bf16ties5", "bf16wide",
+                                  "normal"])
 @pytest.mark.parametrize("N,k,m", [(16384, 1024, 4), (3000, 1024, 4), (700, 32, 4),
                                    (1025, 1024, 4), (40000, 512, 4), (20001, 100, 4),
                                    (262144, 1024, 4)])
@@ -341,6 +347,27 @@ def test_topk_bit_exact(kind, N, k, m):
     # rows over 16384 entries take the multi-block path (workspace); the odd
     # length exercises the unaligned key loads
     L.topk_select(st, fmt, torch.from_numpy(qpos).reshape(rows, 1).to(d),
+                  torch.from_numpy(n_ent).to(d), rows, 1, N, m, k, idx)
+    got = idx.cpu().numpy()[:, 0]
+    for r in range(rows):
+        nv = int(O.n_visible(int(qpos[r]), m, N))
+        want = O.topk(S[r].astype(np.float64), nv, k)
+        np.testing.assert_array_equal(got[r], want, err_msg=f"row {r} nv {nv}")
+
+
+@pytest.mark.parametrize("N,k,rows", [(262144, 1024, 70),    # more rows than one launch pair takes
+                                       (40000, 20000, 3)])     # k above a slice: the per-digit path
+def test_topk_long_bf16_rows_bit_exact(N, k, rows):
+    d = dev()
+    rng = np.random.default_rng(N + k + rows)
+    S = _score_rows(rng, "bf16", rows, N)
+    m = 4
+    qpos = (4 * N - 1 - 4 * rng.integers(0, N, size=rows)).astype(np.int32)
+    qpos[:3] = [4 * N - 1, 4 * k - 1, 4 * k + 3]   # full, exactly k, k + 1 visible
+    n_ent = np.full(rows, N, np.int32)
+    st = torch.from_numpy(S).to(d).to(torch.bfloat16).reshape(rows, 1, N)
+    idx = torch.empty(rows, 1, k, dtype=torch.int32, device=d)
+    L.topk_select(st, L.BF16, torch.from_numpy(qpos).reshape(rows, 1).to(d),
                   torch.from_numpy(n_ent).to(d), rows, 1, N, m, k, idx)
     got = idx.cpu().numpy()[:, 0]
     for r in range(rows):
