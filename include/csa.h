@@ -380,6 +380,36 @@ csa_status hca_attend_paged(const void* q, csa_dtype q_t, const float* q_norm_w,
                             void* out, csa_dtype out_t,
                             void* ws, size_t* ws_bytes, hipStream_t stream);
 
+/*
+ * sparse_mqa_attend_noalloc -- sparse_mqa_attend that allocates nothing and
+ * takes no workspace, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.
+ *
+ *  Arguments, layouts and results are those of sparse_mqa_attend without
+ *  ws / ws_bytes.  The split-softmax partials (sparse_mqa_attend's workspace)
+ *  go to a scratch array of CSA_NOALLOC_SCRATCH_BYTES inside the library's
+ *  device memory, one copy per GPU, held until the process ends.  A call whose
+ *  partials need more returns CSA_ERR_WORKSPACE and launches nothing (32 MiB
+ *  covers, e.g., 32 decode rows x 64 heads or 8 x 128 heads at k = 1024 and a
+ *  128-row window, 8 splits).
+ *  Every call looks up the current device's scratch address the first time
+ *  it runs on that device (CSA_ERR_LAUNCH if the lookup fails); an empty call
+ *  (B == 0) does only that, e.g. before a graph capture.
+ *  All calls on one GPU share its scratch, which keeps the last call's
+ *  contents: calls that overlap in time on one GPU (several streams or host
+ *  threads) race on it and must be serialised by the caller.  Every partial a
+ *  call reads is written by that call first.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+csa_status sparse_mqa_attend_noalloc(const void* q, csa_dtype q_t, const float* q_norm_w,
+                                     float eps, int rope_dims, float rope_theta,
+                                     const int32_t* q_pos, const void* kv, csa_dtype kv_t,
+                                     int Nmax, const int32_t* idx, int k,
+                                     const void* win, int win_len, int n_win,
+                                     const float* sink, float scale, int B, int Tq, int nh,
+                                     int c, void* out, csa_dtype out_t, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

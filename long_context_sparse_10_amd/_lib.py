@@ -64,7 +64,13 @@ SIGNATURES = {
     "hca_attend_paged": [_vp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _i32, _i32, _pp, _vp, _i32,
                          _vp, _i32, _i32, _vp, _f32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _psz,
                          _vp],
+    "sparse_mqa_attend_noalloc": [_vp, _i32, _vp, _f32, _i32, _f32, _vp, _vp, _i32, _i32, _vp,
+                                  _i32, _vp, _i32, _i32, _vp, _f32, _i32, _i32, _i32, _i32, _vp,
+                                  _i32, _vp],
 }
+
+# bytes of the fixed scratch of sparse_mqa_attend_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class Pages:
@@ -240,6 +246,18 @@ def sparse_mqa_attend(q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, k
     st, ws = _workspace(call, q.device, ws)
     _check("sparse_mqa_attend_paged" if ps is not None else "sparse_mqa_attend", st)
     return ws
+
+
+def sparse_mqa_attend_noalloc(q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, kv_t, Nmax,
+                              idx, k, win, win_len, n_win, sink, scale, B, Tq, nh, c, out, out_t,
+                              stream=None):
+    """sparse_mqa_attend with the library's fixed per-GPU scratch: no
+    workspace, no allocation."""
+    st = lib().sparse_mqa_attend_noalloc(
+        _p(q), q_t, _p(q_norm_w), eps, rope_dims, rope_theta, _p(q_pos), _p(kv), kv_t, Nmax,
+        _p(idx), k, _p(win), win_len, n_win, _p(sink), scale, B, Tq, nh, c, _p(out), out_t,
+        _s(stream))
+    _check("sparse_mqa_attend_noalloc", st)
 
 
 def hca_attend(q, q_t, q_norm_w, eps, rope_dims, rope_theta, q_pos, kv, kv_t, Nmax, n_entries,

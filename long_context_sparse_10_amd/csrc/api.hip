@@ -66,6 +66,10 @@ csa_status check_pages(const csa_pages* p, int Nmax, int64_t rb, const void* bas
   return CSA_OK;
 }
 
+}  // namespace
+
+namespace csa {
+
 csa_status check_attend(const AttendArgs& a) {
   if (a.q == nullptr || a.q_pos == nullptr || a.kv == nullptr || a.sink == nullptr ||
       a.out == nullptr)
@@ -91,7 +95,7 @@ csa_status check_attend(const AttendArgs& a) {
   return CSA_OK;
 }
 
-}  // namespace
+}  // namespace csa
 
 extern "C" {
 
@@ -102,7 +106,7 @@ const char* csa_status_string(csa_status s) {
     case CSA_OK: return "ok";
     case CSA_ERR_INVALID: return "invalid argument";
     case CSA_ERR_UNSUPPORTED: return "unsupported dtype combination";
-    case CSA_ERR_WORKSPACE: return "workspace too small";
+    case CSA_ERR_WORKSPACE: return "workspace too small (or over the no-allocation scratch)";
     case CSA_ERR_LAUNCH: return "kernel launch failed";
   }
   return "unknown status";

@@ -98,6 +98,8 @@ struct AttendArgs {
 };
 
 // workspace bytes the attention call needs for these host sizes
+// host checks of every attention argument (api.hip)
+csa_status check_attend(const AttendArgs& a);
 size_t attend_workspace(const AttendArgs& a);
 hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s);
 

@@ -30,7 +30,8 @@ def test_library_loads_and_exports_every_declared_symbol():
                           "csa_compress_append", "indexer_score", "topk_select",
                           "sparse_mqa_attend", "hca_attend", "csa_compress_paged",
                           "csa_compress_append_paged", "indexer_score_paged",
-                          "sparse_mqa_attend_paged", "hca_attend_paged", "grouped_out_proj"}
+                          "sparse_mqa_attend_paged", "hca_attend_paged", "grouped_out_proj",
+                          "sparse_mqa_attend_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -160,6 +161,35 @@ def test_attend_validation():
     assert _attend(sparse=False, mp=0) == _lib.ERR_INVALID
     assert _attend(rd=63) == _lib.ERR_INVALID
     assert _attend(sink=None) == _lib.ERR_INVALID
+
+
+def _noalloc(**kw):
+    a = dict(q=D, qt=L.BF16, qn=None, eps=1e-6, rd=64, th=1e4, qp=D, kv=D, kvt=L.BF16, N=16384,
+             idx=D, k=1024, win=D, wl=128, nw=128, sink=D, scale=0.044, B=32, Tq=1, nh=64, c=512,
+             out=D, ot=L.BF16)
+    a.update(kw)
+    return L.lib().sparse_mqa_attend_noalloc(a["q"], a["qt"], a["qn"], a["eps"], a["rd"], a["th"],
+                                             a["qp"], a["kv"], a["kvt"], a["N"], a["idx"], a["k"],
+                                             a["win"], a["wl"], a["nw"], a["sink"], a["scale"],
+                                             a["B"], a["Tq"], a["nh"], a["c"], a["out"], a["ot"],
+                                             None)
+
+
+def test_noalloc_attend_host_checks():
+    """The no-allocation attention checks its arguments like sparse_mqa_attend
+    and refuses, before touching the GPU, a call whose split partials exceed
+    its fixed scratch (32 MiB)."""
+    assert _noalloc(idx=None) == _lib.ERR_INVALID
+    assert _noalloc(win=None) == _lib.ERR_INVALID
+    assert _noalloc(kvt=L.MXFP4) == _lib.ERR_UNSUPPORTED
+    # partials of 64 rows x 128 heads x 8 splits = 67.6 MB > 32 MiB
+    need = ctypes.c_size_t(0)
+    assert _attend(B=64, nh=128, ws=None, ws_bytes=ctypes.byref(need)) == _lib.OK
+    assert need.value > _lib.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(B=64, nh=128) == _lib.ERR_WORKSPACE
+    # 32 rows x 64 heads (the 64K decode batch) fit
+    assert _attend(B=32, nh=64, ws=None, ws_bytes=ctypes.byref(need)) == _lib.OK
+    assert 0 < need.value <= _lib.NOALLOC_SCRATCH_BYTES
 
 
 def test_attend_workspace_depends_on_slots_not_batch():
