@@ -40,19 +40,16 @@ METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP
 # of known size (--copy-probe).  An entry holds for the kernel source it was
 # taken on (sha256 of the .hip file); after any change it reports null.
 TRAFFIC = {
-    'decode_64k': {"src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 67722.4, "write_kib": 2048.0, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'hca_decode_1m': {"src": "attend.hip", "sha256": "ae43da131e40bab8930d9ee5ceba58df2972325b9233c721d116c4efef778fcf", "fetch_kib": 75822.0, "write_kib": 17536.0, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'decode_1m_fp4': {"src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 69941.2, "write_kib": 4096.0, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'prefill_32k': {"src": "attend.hip", "sha256": "ae43da131e40bab8930d9ee5ceba58df2972325b9233c721d116c4efef778fcf", "fetch_kib": 3574817.2, "write_kib": 2097152.9, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'prefill_32k_mxfp4': {"src": "attend.hip", "sha256": "ae43da131e40bab8930d9ee5ceba58df2972325b9233c721d116c4efef778fcf", "fetch_kib": 3405804.8, "write_kib": 2097155.9, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'oproj_decode': {"src": "oproj.hip", "sha256": "99d8386e33f20e6b4550c52e1cad5985505842be7148f54ce0c4b5e890c9f760", "fetch_kib": 80948.4, "write_kib": 8967.4, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'oproj_prefill': {"src": "oproj.hip", "sha256": "99d8386e33f20e6b4550c52e1cad5985505842be7148f54ce0c4b5e890c9f760", "fetch_kib": 4553178.6, "write_kib": 842469.5, "fetch_scale": 1.9998, "write_scale": 1.0},
 }
 
 
 # ------------------------------------------------------------------ algorithmic bytes
 def decode_bytes(sp, N):
-    """Bytes the method must move per query token (one sequence)."""
+    """Algorithmic bytes per query token (one sequence).  `total` is what the
+    method must move: index keys, the indexer query and weights, the selected
+    KV rows and the window, the query and the output.  The per-stage figures
+    add each kernel's own output and the intermediates it reads (scores,
+    indices), which a fused path would not move."""
     c, d_r = sp.c, sp.d_r
     row = {"bf16": 2 * c, "fp8mix": (c - d_r) + 2 * d_r, "f32": 4 * c}[sp.kv_format]
     q = sp.nh * c * 2
@@ -64,12 +61,21 @@ def decode_bytes(sp, N):
     if sp.index_format == "mxfp4":
         kI = N * (sp.cI // 2 + sp.cI // 32)
         qI = sp.nI * (sp.cI // 2 + sp.cI // 32)
+        score = 2
     else:
         kI = N * sp.cI * 2
         qI = sp.nI * sp.cI * 2
-    indexer = kI + qI + sp.nI * 4
+        score = 4
+    method_indexer = kI + qI + sp.nI * 4
     attend = min(sp.k, N) * row + win + q + out
-    return dict(indexer=indexer, attend=attend, total=indexer + attend)
+    return dict(indexer=method_indexer + N * score, topk=N * score + sp.k * 4, attend=attend,
+                total=method_indexer + attend)
+
+
+# the kernels behind each call of the decode step
+DECODE_KERNELS = {"indexer": "indexer_mfma_kernel",
+                  "topk": "topk_fine_hist_kernel + topk_fine_emit_kernel (2^14 < N); topk_kernel",
+                  "attend": "attend_mfma_kernel + attend_combine_kernel"}
 
 
 def prefill_flops(sp, T):
@@ -82,7 +88,86 @@ def prefill_flops(sp, T):
     return fi, fa
 
 
+# ------------------------------------------------------------------ timing helpers
+def timed_steps(torch, stream, run_step, steps):
+    """K steps back to back on `stream`, one HIP event at each step boundary:
+    (wall seconds, per-step GPU microseconds)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev[0].record(stream)
+        for i in range(steps):
+            run_step(i)
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)])
+
+
+def stage_times(torch, stream, stages, reps):
+    """Each call of the path launched `reps` times back to back (over the
+    rotated inputs) between two HIP events on its launch stream: microseconds
+    per call, the period a call takes in a full queue.  Events between the
+    calls of a step would add their own dispatch gaps (4-7 us per call here);
+    this period matches the kernel trace's durations."""
+    out = {}
+    for name, fn in stages:
+        with torch.cuda.stream(stream):
+            fn(0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                fn(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e3 / reps
+    return out
+
+
+def distribution(us):
+    return dict(median=float(np.median(us)), p10=float(np.percentile(us, 10)),
+                p90=float(np.percentile(us, 90)), mean=float(np.mean(us)))
+
+
+def copy_bandwidth(torch, stream, nbytes=1 << 30, reps=10):
+    """Read + write GB/s of a plain device copy (the streaming rate a kernel can
+    reach), measured here."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    with torch.cuda.stream(stream):
+        b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            b.copy_(a)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbs
+
+
 # ------------------------------------------------------------------ CPU baseline
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return dict(host_cpus=os.cpu_count(), cpus_available=affinity, cpu_model=model,
+                blas_threads=blas_threads())
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -105,7 +190,28 @@ def cpu_baseline_decode(inp, budget_s=12.0):
     dt = time.perf_counter() - t0
     return dict(value=n / dt, unit="query-tokens/s", cores=blas_threads(), kind="oracle",
                 sample=f"{n} query tokens (sequences cycled) of the same workload, fp64 numpy, "
-                       f"{dt:.1f} s")
+                       f"{dt:.1f} s", **host_info())
+
+
+def fp4_recall(inp, gpu_idx, seqs=(0, -1)):
+    """Top-k recall of the timed selection (MXFP4 index keys and queries,
+    bf16 scores) against the fp64 oracle's top-k over the unquantised keys and
+    queries, for a sample of sequences."""
+    from oracle import csa as O
+    sp = inp["spec"]
+    rec = []
+    t0 = time.perf_counter()
+    for b in sorted({s % sp.B for s in seqs}):
+        N, p = int(inp["n_entries"][b]), int(inp["q_pos"][b, 0])
+        nv = int(O.n_visible(p, sp.m, N))
+        ref = set(O.topk(O.index_scores(inp["qI"][b, 0], inp["w"][b, 0], inp["kI"][b], nv),
+                         nv, sp.k).tolist())
+        got = {int(x) for x in gpu_idx[b, 0] if x >= 0}
+        rec.append(len(ref & got) / min(sp.k, nv))
+    return dict(value=float(np.mean(rec)), per_sequence=rec,
+                against="fp64 oracle top-k over the unquantised index keys and queries",
+                seconds=round(time.perf_counter() - t0, 1),
+                context="the pages quote 99.7% for a trained model; these keys are N(0,1)")
 
 
 def cpu_baseline_prefill(inp, rows, budget_s=12.0):
@@ -126,7 +232,8 @@ def cpu_baseline_prefill(inp, rows, budget_s=12.0):
     dt = time.perf_counter() - t1
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
                 sample=f"{done} query rows spread over the sequence (indexer+top-k+attention, "
-                       f"fp64 numpy, {dt:.1f} s; compression done beforehand in {t1 - t0:.1f} s)")
+                       f"fp64 numpy, {dt:.1f} s; compression done beforehand in {t1 - t0:.1f} s)",
+                **host_info())
 
 
 # ------------------------------------------------------------------ decode bench
@@ -161,21 +268,6 @@ def run_decode(args, torch, I, G):
     kinds = ["indexer", "topk", "attend"] if sp.kind == "decode" else ["attend"]
     call = {"indexer": G.decode_indexer, "topk": G.decode_topk,
             "attend": lambda c, s: G.decode_attend(c, stream=s)}
-    # per-kernel launch time: each call back to back over the rotated copies
-    # (the queue stays full, so an event pair brackets kernel time only)
-    avg = {}
-    for kind in kinds:
-        reps = max(args.steps, 12)
-        with torch.cuda.stream(stream):
-            for i in range(len(copies)):
-                call[kind](copies[i], stream)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(reps):
-                call[kind](copies[i % len(copies)], stream)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        avg[kind] = e0.elapsed_time(e1) * 1e3 / reps
     # the step: eager launches (measured faster here than HIP graph replay of
     # the same calls), or one HIP graph per cache copy with --graph
     side = torch.cuda.Stream()
@@ -204,24 +296,32 @@ def run_decode(args, torch, I, G):
         for i in range(args.warmup):
             run_step(i)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start = time.perf_counter()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for i in range(args.steps):
-            run_step(i)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    gpu_ms = e0.elapsed_time(e1)
+    # the timed steps (value, and the distribution of the step)
+    elapsed, step_us = timed_steps(torch, stream, run_step, args.steps)
+    # per-call times: each call back to back over the rotated copies
+    stages = [(kind, (lambda i, k=kind: call[k](copies[i % len(copies)], stream)))
+              for kind in kinds]
+    avg = stage_times(torch, stream, stages, max(args.steps, 12))
+    copy_gbs = copy_bandwidth(torch, stream)
     ms_step = elapsed / args.steps * 1e3
     N = inp["Nmax"]
     by = decode_bytes(sp, N)
-    dom = "indexer" if sp.kind == "decode" else "attend"
+    value = sp.B * args.steps / elapsed
+    dist = distribution(step_us)
+    step_bytes = by["total"] * sp.B
+    step_gbs = step_bytes / (dist["median"] * 1e-6) / 1e9
+    per = {}
+    for k in kinds:
+        gbs = by[k] * sp.B / (avg[k] * 1e-6) / 1e9
+        per[k] = dict(kernels=DECODE_KERNELS[k], us=round(avg[k], 2), bytes=by[k] * sp.B,
+                      achieved_gbs=round(gbs, 1), frac=round(gbs / HBM_PEAK_GBS, 4))
+    # the dominant kernel: the longest single kernel of the step, the indexer
+    # in CSA decode (the attention call is two kernels, each shorter; every
+    # call's own fraction is under roofline_step.kernels); HCA decode has only
+    # the attention call
+    dom = "indexer" if "indexer" in kinds else "attend"
     dom_bytes = by[dom] * sp.B
     achieved = dom_bytes / (avg[dom] * 1e-6) / 1e9
-    value = sp.B * args.steps / elapsed
-    step_gbs = by["total"] * sp.B / (ms_step * 1e-3) / 1e9
     res = dict(
         metric=METRIC, value=value, unit="query-tokens/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms_step, higher_is_better=True, scaling="weak",
@@ -234,16 +334,20 @@ def run_decode(args, torch, I, G):
                     cache=(f"paged: {base.pool.page_bytes}-byte pages of 32 CSA rows + 32 index "
                            "keys + 1 HCA row, random page order" if base.pool is not None
                            else "dense")),
-        roofline=dict(bound="hbm", kernel=dom, achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=achieved / HBM_PEAK_GBS, traffic=None,
-                      algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=avg[dom]),
-        step=dict(algorithmic_bytes=by["total"] * sp.B, achieved_gbs=step_gbs,
-                  frac_of_hbm_peak=step_gbs / HBM_PEAK_GBS, gpu_ms_per_step=gpu_ms / args.steps,
-                  launch=("HIP graph per cache copy" if args.graph else "eager launches")
-                  + (f"; batch in {args.chunks} groups on 2 streams" if args.chunks > 1 else ""),
-                  kernel_us={k: round(v, 2) for k, v in avg.items()}),
+        roofline=dict(bound="hbm", kernel=DECODE_KERNELS[dom], achieved=achieved,
+                      peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS, traffic=None,
+                      algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=avg[dom],
+                      timing="HIP events around back-to-back launches of the call over the "
+                             "rotated copies, on its launch stream, after the timed steps"),
+        roofline_step=dict(bound="hbm", achieved=step_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                           frac=step_gbs / HBM_PEAK_GBS, algorithmic_bytes=step_bytes,
+                           step_us=dist, copy_gbs=round(copy_gbs, 1),
+                           frac_of_copy=step_gbs / copy_gbs, kernels=per,
+                           launch=("HIP graph per cache copy" if args.graph else "eager launches")
+                           + (f"; batch in {args.chunks} groups on 2 streams"
+                              if args.chunks > 1 else "")),
     )
-    return res, inp
+    return res, (inp, copies[0])
 
 
 # ------------------------------------------------------------------ output projection
@@ -328,7 +432,8 @@ def cpu_baseline_oproj(case, budget_s=10.0):
             break
     dt = time.perf_counter() - t0
     return dict(value=n / dt, unit="query-tokens/s", cores=blas_threads(), kind="oracle",
-                sample=f"{n} rows ({rows} per call) of the same shape, fp64 numpy, {dt:.1f} s")
+                sample=f"{n} rows ({rows} per call) of the same shape, fp64 numpy, {dt:.1f} s",
+                **host_info())
 
 
 # ------------------------------------------------------------------ prefill bench
@@ -348,7 +453,6 @@ def run_prefill(args, torch, I, G):
         G.prefill_attention_path(p, stream)
     torch.cuda.synchronize()
     t_comp = e0.elapsed_time(e1)
-    kinds = ["indexer", "topk", "attend"]
     n = sp.T // sp.m
     for _ in range(args.warmup):
         with torch.cuda.stream(stream):
@@ -356,30 +460,32 @@ def run_prefill(args, torch, I, G):
     torch.cuda.synchronize()
     import long_context_sparse_10_amd as L
     sfmt = L.BF16 if sp.index_format == "mxfp4" else L.F32
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t_start = time.perf_counter()
     scale = 1.0 / math.sqrt(sp.c)
-    with torch.cuda.stream(stream):
-        for i in range(args.steps):
-            e = ev[i]
-            e[0].record(stream)
-            G.prefill_indexer(p, stream)
-            e[1].record(stream)
-            L.topk_select(p.scores, sfmt, p.q_pos, p.n_entries, 1, sp.T, n, sp.m, sp.k, p.idx,
-                          None, stream)
-            e[2].record(stream)
-            L.sparse_mqa_attend(p.q, L.BF16, p.gamma, 1e-6, sp.d_r, 1e4, p.q_pos, p.kv, L.BF16, n,
-                                p.idx, sp.k, p.win, sp.T, sp.n_win, p.sink, scale, 1, sp.T, sp.nh,
-                                sp.c, p.out, L.BF16, p.ws_attend, stream)
-            e[3].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    avg = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) * 1e3
-           for j, k in enumerate(kinds)}
+    elapsed, step_us = timed_steps(torch, stream, lambda i: G.prefill_attention_path(p, stream),
+                                   args.steps)
+    stages = [
+        ("indexer", lambda i: G.prefill_indexer(p, stream)),
+        ("topk", lambda i: L.topk_select(p.scores, sfmt, p.q_pos, p.n_entries, 1, sp.T, n, sp.m,
+                                         sp.k, p.idx, None, stream)),
+        ("attend", lambda i: L.sparse_mqa_attend(p.q, L.BF16, p.gamma, 1e-6, sp.d_r, 1e4, p.q_pos,
+                                                 p.kv, L.BF16, n, p.idx, sp.k, p.win, sp.T,
+                                                 sp.n_win, p.sink, scale, 1, sp.T, sp.nh, sp.c,
+                                                 p.out, L.BF16, p.ws_attend, stream)),
+    ]
+    avg = stage_times(torch, stream, stages, args.steps)
     fi, fa = prefill_flops(sp, sp.T)
     ms = elapsed / args.steps * 1e3
     tflops = (fi + fa) / (ms * 1e-3) / 1e12
+    dist = distribution(step_us)
+    step_tf = (fi + fa) / (dist["median"] * 1e-6) / 1e12
     att = fa / (avg["attend"] * 1e-6) / 1e12
+    idx_tf = fi / (avg["indexer"] * 1e-6) / 1e12
+    per = dict(indexer=dict(kernels="indexer_rows_kernel", us=round(avg["indexer"], 1),
+                            flops=fi, tflops=round(idx_tf, 1),
+                            frac=round(idx_tf / BF16_PEAK_TFLOPS, 4)),
+               topk=dict(kernels="topk_kernel", us=round(avg["topk"], 1)),
+               attend=dict(kernels="attend_pf_kernel", us=round(avg["attend"], 1), flops=fa,
+                           tflops=round(att, 1), frac=round(att / BF16_PEAK_TFLOPS, 4)))
     res = dict(
         metric=METRIC, value=tflops, unit="TFLOP/s", n_gpus=1, steps=args.steps,
         warmup=args.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak",
@@ -387,20 +493,64 @@ def run_prefill(args, torch, I, G):
         data="synthetic",
         config=dict(workload=sp.name, seq_len=sp.T, hidden=sp.d, heads=sp.nh, head_dim=sp.c,
                     top_k=sp.k, indexer=f"{sp.nI}x{sp.cI} {sp.index_format}", window=sp.n_win),
-        roofline=dict(bound="mfma", kernel="attend", achieved=att, peak=BF16_PEAK_TFLOPS,
-                      unit="TFLOP/s", frac=att / BF16_PEAK_TFLOPS, traffic=None,
-                      algorithmic_flops_per_launch=fa, avg_launch_us=avg["attend"]),
-        step=dict(indexer_tflops=fi / (avg["indexer"] * 1e-6) / 1e12,
-                  attend_tflops=att, kernel_us={k: round(v, 1) for k, v in avg.items()},
-                  compress_ms_untimed=t_comp),
+        roofline=dict(bound="mfma", kernel="attend_pf_kernel", achieved=att,
+                      peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=att / BF16_PEAK_TFLOPS,
+                      traffic=None, algorithmic_flops_per_launch=fa, avg_launch_us=avg["attend"],
+                      timing="HIP events around back-to-back launches of the call, on its "
+                             "launch stream, after the timed steps"),
+        roofline_step=dict(bound="mfma", achieved=step_tf, peak=BF16_PEAK_TFLOPS,
+                           unit="TFLOP/s", frac=step_tf / BF16_PEAK_TFLOPS,
+                           algorithmic_flops=fi + fa, step_us=dist, kernels=per,
+                           compress_ms_untimed=t_comp),
     )
     return res, inp
 
 
-def kernel_traffic(config):
-    """Measured HBM bytes per launch of the roofline kernel, or None."""
+# ------------------------------------------------------------------ tiny configurations
+def run_tiny(args, torch, I, G):
+    """Tiny CSA / HCA: one sequence of 1024 tokens, hidden 256, fp32.  A step is
+    the whole path: compression (main KV, index keys, window rows), then
+    indexer, top-k and sparse attention (CSA) or dense attention (HCA).  Time
+    only: every kernel runs a few microseconds, launch latency decides."""
+    sp = I.CONFIGS[args.config]
+    dev = torch.device("cuda", 0)
+    inp = I.prefill_inputs(sp)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        p = G.upload_prefill(inp, dev)
+
+    def step(i):
+        G.prefill_compress(p, stream)
+        G.prefill_attention_path(p, stream)
+    with torch.cuda.stream(stream):
+        for i in range(max(args.warmup, 1)):
+            step(i)
+    torch.cuda.synchronize()
+    elapsed, step_us = timed_steps(torch, stream, step, args.steps)
+    stages = [("compress", lambda i: G.prefill_compress(p, stream)),
+              ("attention_path", lambda i: G.prefill_attention_path(p, stream))]
+    avg = stage_times(torch, stream, stages, args.steps)
+    ms = elapsed / args.steps * 1e3
+    res = dict(
+        metric=METRIC, value=sp.T / (ms * 1e-3), unit="tokens/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak",
+        vs_baseline=None, dtype="f32", data="synthetic",
+        config=dict(workload=sp.name, seq_len=sp.T, hidden=sp.d, heads=sp.nh, head_dim=sp.c,
+                    rope_dims=sp.d_r, m=sp.m, top_k=sp.k or None,
+                    indexer=(f"{sp.nI}x{sp.cI} f32" if sp.nI else None), window=sp.n_win),
+        roofline=None,
+        step=dict(step_us=distribution(step_us), kernel_us={k: round(v, 1) for k, v in avg.items()},
+                  note="time only: launch-latency bound at this size"),
+        cpu_baseline=None,
+    )
+    return res
+
+
+def kernel_traffic(config, kernel):
+    """Measured HBM bytes per launch of the roofline kernel, or None (no
+    counters for this kernel, or its source changed since they were taken)."""
     t = TRAFFIC.get(config)
-    if t is None:
+    if t is None or t.get("kernel") != kernel:
         return None
     import hashlib
     src = os.path.join(ROOT, "long_context_sparse_10_amd", "csrc", t["src"])
@@ -430,7 +580,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="decode_64k",
                     choices=["decode_64k", "hca_decode_1m", "decode_1m_fp4", "prefill_32k",
-                             "prefill_32k_mxfp4", "oproj_decode", "oproj_prefill"])
+                             "prefill_32k_mxfp4", "oproj_decode", "oproj_prefill", "tiny_csa",
+                             "tiny_hca"])
     ap.add_argument("--copies", type=int, default=6, help="cache copies rotated (cold cache)")
     ap.add_argument("--graph", action="store_true", help="decode: replay each step as a HIP graph")
     ap.add_argument("--chunks", type=int, default=1,
@@ -452,9 +603,12 @@ def main():
         return
     import csa_inputs as I
     from long_context_sparse_10_amd import pipeline as G
+    if args.config.startswith("tiny"):
+        print(json.dumps(run_tiny(args, torch, I, G)), flush=True)
+        return
     if args.config in OPROJ:
         res, case = run_oproj(args, torch)
-        res["roofline"]["traffic"] = kernel_traffic(args.config)
+        res["roofline"]["traffic"] = kernel_traffic(args.config, res["roofline"]["kernel"])
         res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_oproj(case)
         print(json.dumps(res), flush=True)
         return
@@ -462,16 +616,20 @@ def main():
         args.copies = 1
         res, inp = run_prefill(args, torch, I, G)
     else:
-        res, inp = run_decode(args, torch, I, G)
-    res["roofline"]["traffic"] = kernel_traffic(args.config)
+        res, (inp, first) = run_decode(args, torch, I, G)
+    res["roofline"]["traffic"] = kernel_traffic(args.config, res["roofline"]["kernel"])
     if not args.no_cpu_baseline:
         if args.config.startswith("prefill"):
             rows = np.linspace(0, inp["T"] - 1, 64).astype(int)
             res["cpu_baseline"] = cpu_baseline_prefill(inp, rows)
         else:
             res["cpu_baseline"] = cpu_baseline_decode(inp)
+            if inp["spec"].index_format == "mxfp4":
+                res["recall"] = fp4_recall(inp, first.idx.cpu().numpy())
     else:
         res["cpu_baseline"] = None
+        if not args.config.startswith("prefill") and inp["spec"].index_format == "mxfp4":
+            res["recall"] = None
     print(json.dumps(res), flush=True)
 
 

@@ -63,14 +63,23 @@ typedef enum csa_status {
   CSA_ERR_INVALID = 1,
   CSA_ERR_UNSUPPORTED = 2,
   CSA_ERR_WORKSPACE = 3,
-  CSA_ERR_LAUNCH = 4
+  CSA_ERR_LAUNCH = 4,
+  /* range markers, never returned: every int is a value of the type, so
+   * csa_status_string takes any code */
+  CSA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  CSA_STATUS_RANGE_MAX_ = 2147483647
 } csa_status;
 
 typedef enum csa_dtype {
   CSA_F32 = 0,
   CSA_BF16 = 1,
   CSA_FP8MIX = 2,
-  CSA_MXFP4 = 3
+  CSA_MXFP4 = 3,
+  /* range markers, not formats: they make every int a value of the type, so
+   * an unknown code passed across the ABI is rejected (CSA_ERR_UNSUPPORTED)
+   * rather than being an out-of-range enum inside the library */
+  CSA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  CSA_DTYPE_RANGE_MAX_ = 2147483647
 } csa_dtype;
 
 /* Library version string (static storage). */

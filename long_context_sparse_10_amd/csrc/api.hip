@@ -108,6 +108,7 @@ const char* csa_status_string(csa_status s) {
     case CSA_ERR_UNSUPPORTED: return "unsupported dtype combination";
     case CSA_ERR_WORKSPACE: return "workspace too small (or over the no-allocation scratch)";
     case CSA_ERR_LAUNCH: return "kernel launch failed";
+    default: break;
   }
   return "unknown status";
 }

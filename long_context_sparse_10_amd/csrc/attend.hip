@@ -583,10 +583,12 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
       STG[i] = *reinterpret_cast<const u32x4*>(src[i] + 16 * ch);                            \
   }
 #define CSA_COMMIT(STG, OK, BUF)                                                             \
-  if ((OK) == 0xFFu) {                                                                       \
-    CSA_COMMIT_ROWS(STG, 0xFFu, BUF)                                                         \
-  } else {                                                                                   \
-    CSA_COMMIT_ROWS(STG, OK, BUF)                                                            \
+  {                                                                                          \
+    if ((OK) == 0xFFu) {                                                                     \
+      CSA_COMMIT_ROWS(STG, 0xFFu, BUF)                                                       \
+    } else {                                                                                 \
+      CSA_COMMIT_ROWS(STG, OK, BUF)                                                          \
+    }                                                                                        \
   }
   /* (a full set of rows needs no per-row zeroing) */
 #define CSA_COMMIT_ROWS(STG, OK, BUF)                                                        \

@@ -162,6 +162,7 @@ __host__ __device__ inline int64_t row_bytes(csa_dtype t, int c, int rope_dims) 
     case CSA_BF16: return 2ll * c;
     case CSA_FP8MIX: return (int64_t)(c - rope_dims) + 2ll * rope_dims;
     case CSA_MXFP4: return c / 2;
+    default: break;
   }
   return 0;
 }

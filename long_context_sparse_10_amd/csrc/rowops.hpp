@@ -82,6 +82,7 @@ __device__ void finish_row(float* row, int c, const float* __restrict__ norm_w, 
       }
       break;
     }
+    default: break;  // formats are checked on the host
   }
 }
 
