@@ -12,9 +12,14 @@ below the 256 MiB Infinity Cache, so the timed steps rotate through several
 copies of the caches at distinct addresses (cold-cache protocol).
 
 Prints ONE JSON line.  ``value`` = query tokens/s (decode) or TFLOP/s
-(prefill).  ``roofline`` rates the dominant kernel against its bound, from HIP
-events on the launch stream; ``cpu_baseline`` times the fp64 oracle on a
-bounded sample of the same workload on this host.
+(prefill).  ``roofline`` rates the longest single kernel of the step against
+its bound (per-call time from HIP events around back-to-back launches on the
+launch stream); ``roofline_step`` rates the whole step (median of per-step
+event times) against the same peak and a measured device-copy rate, with each
+call's own fraction; ``cpu_baseline`` times the fp64 oracle on a bounded
+sample of the same workload on this host (with the host's CPU count and
+model), and the MXFP4 workload adds the top-k recall against the fp64
+oracle.  ``tiny_csa`` / ``tiny_hca`` report time only.
 """
 from __future__ import annotations
 
@@ -40,6 +45,11 @@ METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP
 # of known size (--copy-probe).  An entry holds for the kernel source it was
 # taken on (sha256 of the .hip file); after any change it reports null.
 TRAFFIC = {
+    'decode_64k': {"kernel": "indexer_mfma_kernel", "src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 67722.5, "write_kib": 2048.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'decode_1m_fp4': {"kernel": "indexer_mfma_kernel", "src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 69941.3, "write_kib": 4096.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'prefill_32k': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "9181e153bd01382fd35b48e026b25dcde957252e1d45b25e491708041b0930d4", "fetch_kib": 3331267.5, "write_kib": 2097155.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'prefill_32k_mxfp4': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "9181e153bd01382fd35b48e026b25dcde957252e1d45b25e491708041b0930d4", "fetch_kib": 3362582.3, "write_kib": 2097154.3, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'hca_decode_1m': {"kernel": "attend_mfma_kernel + attend_combine_kernel", "src": "attend.hip", "sha256": "9181e153bd01382fd35b48e026b25dcde957252e1d45b25e491708041b0930d4", "fetch_kib": 75732.5, "write_kib": 17536.0, "fetch_scale": 1.9998, "write_scale": 1.0},
 }
 
 
