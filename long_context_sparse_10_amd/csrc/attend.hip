@@ -241,6 +241,7 @@ struct AttendSmem {
   uint32_t vmask[AT_TAB / 32 + 2];
   float rcs[AT_C / 2][2];           // cos / sin of the query position for each RoPE pair
   f32x4 qc[AT_C / 2];               // query coefficients per channel pair (see attend_mfma_kernel)
+  float gq[AT_C];                   // the same outside the RoPE channels: gain x tau x log2 e
 };
 
 // load 8 consecutive elements (dims d..d+7) of a q row as fp32
@@ -441,7 +442,7 @@ __device__ __forceinline__ void attend_store_out(const AttendArgs& a, int row, i
 //    registers, up to two tiles ahead of the one being committed, and commits
 //    them (expanding e4m3 to bf16) to the LDS tile the math waves are not using.
 // One barrier per tile separates the two buffers.
-template <int KVF>
+template <int KVF, bool QBF16>
 __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt, int chunk,
                                                          int nsplit, void* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) AttendSmem sm;
@@ -489,6 +490,9 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
     const float g0 = a.q_norm_w != nullptr ? a.q_norm_w[2 * p] : 1.f;
     const float g1 = a.q_norm_w != nullptr ? a.q_norm_w[2 * p + 1] : 1.f;
     sm.qc[p] = f32x4{g0 * cs * qscale, g1 * sn * qscale, g0 * sn * qscale, g1 * cs * qscale};
+    // a pair outside the RoPE channels has coefficients (g0 qscale, 0, 0, g1 qscale)
+    sm.gq[2 * p] = g0 * 1.f * qscale;
+    sm.gq[2 * p + 1] = g1 * 1.f * qscale;
   }
   // ---- slot table and per-tile validity masks (one coalesced pass)
   for (int i = tid; i < ((ntiles * AT_TILE + 63) & ~63); i += 512) {
@@ -509,37 +513,71 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   // later reads back as its operand; kept in shared memory, they can be
   // re-read instead of held through the tile loop.
 #define CSA_QPREP()                                                                          \
-  {                                                                                          \
+  if constexpr (QBF16) {                                                                     \
+    /* the wave's 16 raw query rows, coalesced: load i takes head 16 mw + i, lane l its */   \
+    /* bytes 16 l .. 16 l + 15, into the wave's own rows of sm.Q; the same wave reads */     \
+    /* them back in the operand layout (LDS keeps one wave's accesses in order).  The */    \
+    /* query dtype is a template parameter so that these loops stay free of branches. */   \
     u32x4 qraw[16];                                                                          \
-    if (a.q_t == CSA_BF16) {                                                                 \
-      _Pragma("unroll") for (int ks = 0; ks < 16; ++ks)                                      \
-        qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 2 * (128 * g + 8 * ks));           \
-    }                                                                                        \
+    const uint8_t* qb = (const uint8_t*)a.q + ((int64_t)row * a.nh + 64 * hg + 16 * mw) * (2 * AT_C); \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i)                                           \
+      qraw[i] = *reinterpret_cast<const u32x4*>(qb + (int64_t)i * (2 * AT_C) + 16 * lane);     \
+    _Pragma("unroll") for (int i = 0; i < 16; ++i)                                           \
+      *reinterpret_cast<u32x4*>(&sm.Q[16 * mw + i][8 * lane]) = qraw[i];                    \
+    _Pragma("unroll") for (int ks = 0; ks < 16; ++ks)                                        \
+      qraw[ks] = *reinterpret_cast<const u32x4*>(&sm.Q[16 * mw + li][128 * g + 8 * ks]);     \
+    /* sum of squares straight from the packed bf16 pairs (v_dot2) */                        \
     float ssp[4] = {0.f, 0.f, 0.f, 0.f};                                                     \
-    _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                      \
-      if (a.q_t == CSA_BF16) {                                                               \
-        /* sum of squares straight from the packed bf16 pairs (v_dot2) */                    \
-        ssp[ks & 3] = sumsq_bf16x8(qraw[ks], ssp[ks & 3]);                                   \
-      } else {                                                                               \
-        float v[8];                                                                          \
-        load8(qrow, a.q_t, 128 * g + 8 * ks, v);                                             \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i) ssp[ks & 3] = fmaf(v[i], v[i], ssp[ks & 3]); \
-      }                                                                                      \
-    }                                                                                        \
+    _Pragma("unroll") for (int ks = 0; ks < 16; ++ks)                                        \
+      ssp[ks & 3] = sumsq_bf16x8(qraw[ks], ssp[ks & 3]);                                     \
     float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);                                        \
+    ss += __shfl_xor(ss, 16);                                                                \
+    ss += __shfl_xor(ss, 32);                                                                \
+    const float inv = 1.0f / sqrtf(ss / (float)AT_C + a.eps);                                \
+    /* lane group 3 holds the last channels: a chunk ks can hold RoPE channels only */    \
+    /* when 384 + 8 ks + 8 > c - d_r (the same test for every lane).  There every lane */    \
+    /* takes the pair coefficients; elsewhere the pair form reduces to x g qscale. */        \
+    _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                      \
+      u32x4 pk;                                                                              \
+      if (392 + 8 * ks > AT_C - d_r) {                                                       \
+        const f32x4* c4 = &sm.qc[(128 * g + 8 * ks) >> 1];                                   \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+          const f32x4 c = c4[i];                                                             \
+          const float x0 = __uint_as_float(qraw[ks][i] << 16) * inv;                         \
+          const float x1 = __uint_as_float(qraw[ks][i] & 0xFFFF0000u) * inv;                 \
+          pk[i] = pack_bf16x2_hw(fmaf(c[0], x0, -c[1] * x1), fmaf(c[2], x0, c[3] * x1));     \
+        }                                                                                    \
+      } else if (a.q_norm_w != nullptr) {                                                    \
+        const f32x4 ga = *reinterpret_cast<const f32x4*>(&sm.gq[128 * g + 8 * ks]);          \
+        const f32x4 gb = *reinterpret_cast<const f32x4*>(&sm.gq[128 * g + 8 * ks + 4]);      \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+          const f32x4 gg = i < 2 ? ga : gb;                                                  \
+          const float x0 = __uint_as_float(qraw[ks][i] << 16) * inv;                         \
+          const float x1 = __uint_as_float(qraw[ks][i] & 0xFFFF0000u) * inv;                 \
+          pk[i] = pack_bf16x2_hw(gg[2 * (i & 1)] * x0, gg[2 * (i & 1) + 1] * x1);            \
+        }                                                                                    \
+      } else {                                                                               \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
+          const float x0 = __uint_as_float(qraw[ks][i] << 16) * inv;                         \
+          const float x1 = __uint_as_float(qraw[ks][i] & 0xFFFF0000u) * inv;                 \
+          pk[i] = pack_bf16x2_hw((1.f * qscale) * x0, (1.f * qscale) * x1);                  \
+        }                                                                                    \
+      }                                                                                      \
+      *reinterpret_cast<u32x4*>(&sm.Q[16 * mw + li][128 * g + 8 * ks]) = pk;                 \
+    }                                                                                        \
+  } else {                                                                                   \
+    float ss = 0.f;                                                                          \
+    _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                      \
+      float v[8];                                                                            \
+      load8(qrow, a.q_t, 128 * g + 8 * ks, v);                                               \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);               \
+    }                                                                                        \
     ss += __shfl_xor(ss, 16);                                                                \
     ss += __shfl_xor(ss, 32);                                                                \
     const float inv = 1.0f / sqrtf(ss / (float)AT_C + a.eps);                                \
     _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                      \
       float v[8];                                                                            \
-      if (a.q_t == CSA_BF16) {                                                               \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                      \
-          v[2 * i] = __uint_as_float(qraw[ks][i] << 16);                                     \
-          v[2 * i + 1] = __uint_as_float(qraw[ks][i] & 0xFFFF0000u);                         \
-        }                                                                                    \
-      } else {                                                                               \
-        load8(qrow, a.q_t, 128 * g + 8 * ks, v);                                             \
-      }                                                                                      \
+      load8(qrow, a.q_t, 128 * g + 8 * ks, v);                                               \
       const f32x4* c4 = &sm.qc[(128 * g + 8 * ks) >> 1];                                     \
       u32x4 pk;                                                                              \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                        \
@@ -1014,10 +1052,15 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s) {
   const int64_t rows8 = (rows + 7) / 8 * 8;
   dim3 grid((unsigned)((int64_t)nsplit * (a.nh / 64) * rows8));
   void* w = ws;
-  if (a.kv_t == CSA_BF16)
-    hipLaunchKernelGGL(attend_mfma_kernel<CSA_BF16>, grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+  const bool qb = a.q_t == CSA_BF16;
+  if (a.kv_t == CSA_BF16 && qb)
+    hipLaunchKernelGGL((attend_mfma_kernel<CSA_BF16, true>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+  else if (a.kv_t == CSA_BF16)
+    hipLaunchKernelGGL((attend_mfma_kernel<CSA_BF16, false>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+  else if (qb)
+    hipLaunchKernelGGL((attend_mfma_kernel<CSA_FP8MIX, true>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   else
-    hipLaunchKernelGGL(attend_mfma_kernel<CSA_FP8MIX>, grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+    hipLaunchKernelGGL((attend_mfma_kernel<CSA_FP8MIX, false>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   if (nsplit > 1)
     hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)(rows8 * a.nh)),
                        dim3((a.c / 2 + 63) / 64 * 64), 0, s, a, rt, nsplit, (const void*)w);
