@@ -735,11 +735,18 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
     // its rows, so bf16 costs at most 2^-9 of the largest row value.
     const int64_t rs = (int64_t)row * nsplit + split;
     const float il = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    uint16_t* wo = reinterpret_cast<uint16_t*>(ws) + (rs * a.nh + head) * AT_C;
+    // staged through the wave's own 16 rows of sm.Q (its queries are in
+    // registers now), then written one 1 KB head row per instruction; the
+    // same wave reads back what it wrote (LDS keeps its accesses in order)
 #pragma unroll
     for (int nd = 0; nd < 32; ++nd)
-      *reinterpret_cast<uint2*>(wo + 16 * nd + 4 * g) =
+      *reinterpret_cast<uint2*>(&sm.Q[16 * mw + li][16 * nd + 4 * g]) =
           make_uint2(pack_bf16x2_hw(O[nd][0] * il, O[nd][1] * il), pack_bf16x2_hw(O[nd][2] * il, O[nd][3] * il));
+    uint16_t* wo = reinterpret_cast<uint16_t*>(ws) + (rs * a.nh + 64 * hg + 16 * mw) * AT_C;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<u32x4*>(wo + (int64_t)i * AT_C + 8 * lane) =
+          *reinterpret_cast<const u32x4*>(&sm.Q[16 * mw + i][8 * lane]);
     if (g == 0) {
       const int64_t nrows = (int64_t)a.B * a.Tq;
       float* wml = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(ws) + nrows * nsplit * a.nh * AT_C) +
