@@ -301,15 +301,20 @@ __device__ __forceinline__ u32x2 tr_read2(const uint16_t* p) {
 // denominator, the row is normalised, and its RoPE channels are rotated back
 // by -q (rcs holds cos / sin of the query position per RoPE pair).  The lane
 // holds O^T[dim 16nd + 4g + r][head] in log2-unit softmax state (m_run, l_tot).
+// `stage` (bf16 output only; may be null): the wave's 16 rows of AT_LDX in
+// shared memory, free to overwrite; the rows are then written one 1 KB head
+// row per instruction (the same wave reads back what it wrote)
 __device__ __forceinline__ void attend_store_out(const AttendArgs& a, int row, int head, int g,
                                                  const f32x4* O, float m_run, float l_tot,
-                                                 const float (*rcs)[2]) {
+                                                 const float (*rcs)[2], uint16_t* stage = nullptr) {
   const int d_r = a.rope_dims;
   const float z = a.sink[head] * kLog2e;  // sink in log2 units
   const float M = fmaxf(m_run, z);
   const float em = exp2f_hw(m_run - M);
   const float f = em / (l_tot * em + exp2f_hw(z - M));
   uint8_t* orow = (uint8_t*)a.out + ((int64_t)row * a.nh + head) * row_bytes(a.out_t, AT_C, 0);
+  const bool staged = stage != nullptr && a.out_t == CSA_BF16;
+  const int lane = threadIdx.x & 63, li = lane & 15;
 #pragma unroll
   for (int nd = 0; nd < 32; ++nd) {
     const int d0 = 16 * nd + 4 * g;
@@ -330,10 +335,21 @@ __device__ __forceinline__ void attend_store_out(const AttendArgs& a, int row, i
     }
     if (a.out_t == CSA_F32) {
       *reinterpret_cast<f32x4*>(orow + 4 * d0) = f32x4{v[0], v[1], v[2], v[3]};
+    } else if (staged) {
+      *reinterpret_cast<uint2*>(stage + li * AT_LDX + d0) =
+          make_uint2(pack_bf16x2_hw(v[0], v[1]), pack_bf16x2_hw(v[2], v[3]));
     } else {
       *reinterpret_cast<uint2*>(orow + 2 * d0) =
           make_uint2(pack_bf16x2_hw(v[0], v[1]), pack_bf16x2_hw(v[2], v[3]));
     }
+  }
+  if (staged) {
+    // head - li is the wave's first head; its 16 rows are consecutive in out
+    uint16_t* o0 = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)row * a.nh + head - li) * AT_C;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<u32x4*>(o0 + (int64_t)i * AT_C + 8 * lane) =
+          *reinterpret_cast<const u32x4*>(stage + i * AT_LDX + 8 * lane);
   }
 }
 
@@ -728,7 +744,7 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (nsplit == 1) {
-    attend_store_out(a, row, head, g, O, m_run, l_tot, sm.rcs);
+    attend_store_out(a, row, head, g, O, m_run, l_tot, sm.rcs, &sm.Q[16 * mw][0]);
   } else {
     // partials: O / l in bf16 [rows, nsplit, nh, 512], then (m, l) fp32
     // [rows, nsplit, nh, 2].  Each split's O / l is a convex combination of
@@ -939,7 +955,10 @@ __global__ __launch_bounds__(256, 2) void attend_pf_kernel(AttendArgs a, Rope rt
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  attend_store_out(a, row, head, g, O, m_run, l_tot, sm.rcs);
+  // every wave is done with the last tile: the tile buffers stage the output
+  // (wave w takes rows 16 w .. 16 w + 15 of the 64)
+  __syncthreads();
+  attend_store_out(a, row, head, g, O, m_run, l_tot, sm.rcs, &sm.X[0][0][0] + 16 * w * AT_LDX);
 }
 #undef CSA_TILE
 
