@@ -72,17 +72,42 @@ __device__ __forceinline__ void load_keys16(const void* srow, int s0, int nv, in
     if (s0 + i >= nv) key[i] = 0u;
 }
 
-// exclusive block scan of one int per thread; *total gets the block sum.
-// `ws` is LDS of >= 16 ints.  Every thread of the block must call.
+// Wave-wide helpers on DPP row moves (no LDS round trips); every lane of the
+// wave must be active.  DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] =
+// 0x4E, row_ror:n = 0x120 + n, row_shr:n = 0x110 + n.
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int wave_all_max(int x) {
+  x = max(x, dpp_move<0xB1>(x));
+  x = max(x, dpp_move<0x4E>(x));
+  x = max(x, dpp_move<0x124>(x));
+  x = max(x, dpp_move<0x128>(x));  // every lane holds its row's maximum
+  const int a = max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
+  const int b = max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48));
+  return max(a, b);
+}
+__device__ __forceinline__ int wave_all_min(int x) { return -wave_all_max(-x); }
+// inclusive prefix sum over the lanes of the wave
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += dpp_move<0x111>(x);
+  x += dpp_move<0x112>(x);
+  x += dpp_move<0x114>(x);
+  x += dpp_move<0x118>(x);  // prefix within each row of 16 lanes
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int lane = threadIdx.x & 63;
+  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
+// exclusive block scan of one int per thread; *total gets the block sum.  `ws`
+// is LDS of >= 16 ints, not written again before a later barrier (one barrier
+// here).  Every thread of the block must call.
 __device__ __forceinline__ int block_scan_excl(int v, int* ws, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(x, o);
-    if (lane >= o) x += t;
-  }
-  if (lane == 63) ws[wave] = x;
+  const int incl = wave_incl_sum(v);
+  if (lane == 63) ws[wave] = incl;
   __syncthreads();
   int pre = 0, tot = 0;
   for (int i = 0; i < nw; ++i) {
@@ -90,9 +115,8 @@ __device__ __forceinline__ int block_scan_excl(int v, int* ws, int* total) {
     pre += (i < wave) ? y : 0;
     tot += y;
   }
-  __syncthreads();
   *total = tot;
-  return x - v + pre;
+  return incl - v + pre;
 }
 
 // Locate the digit of the `remaining`-th largest key among the keys counted in
@@ -153,17 +177,12 @@ __device__ __forceinline__ void find_digit_block(const int* hist, int nbins, int
   }
 }
 
-// exclusive prefix of one int per lane within the wave; *total gets the wave sum
+// exclusive prefix of one int per lane within the wave; *total gets the wave
+// sum.  Every lane of the wave must call.
 __device__ __forceinline__ int wave_scan_excl(int v, int* total) {
-  const int lane = threadIdx.x & 63;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(x, o);
-    if (lane >= o) x += t;
-  }
-  *total = __shfl(x, 63);
-  return x - v;
+  const int incl = wave_incl_sum(v);
+  *total = __builtin_amdgcn_readlane(incl, 63);
+  return incl - v;
 }
 
 // candidates compacted for the last digits (more go the block-wide way): a
@@ -174,11 +193,10 @@ constexpr int TK_CAND_CAP = 2048;
 // GPU: a 16 KB histogram lets four 512-thread blocks reside per CU instead of
 // three).  bf16 keys take 10 then 6 bits.
 template <bool BF16, int W1>
-__global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ scores,
-                                                    const int32_t* __restrict__ q_pos,
-                                                    const int32_t* __restrict__ n_entries, int Tq,
-                                                    int Nmax, int m, int k, int vec,
-                                                    int32_t* __restrict__ idx) {
+__device__ __forceinline__ void topk_row(const void* __restrict__ scores,
+                                         const int32_t* __restrict__ q_pos,
+                                         const int32_t* __restrict__ n_entries, int Tq, int Nmax,
+                                         int m, int k, int vec, int32_t* __restrict__ idx) {
   __shared__ int hist[BF16 ? 1024 : (1 << W1)];
   extern __shared__ uint32_t cand[];  // [min(16 * blockDim, TK_CAND_CAP)]: keys sharing the k-th's first digit
   __shared__ int scan_ws[16];
@@ -187,26 +205,42 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
   const int row = blockIdx.x, b = row / Tq;
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
   const int cap = min(16 * nt, TK_CAND_CAP);
-  const int nv = min(min(n_entries[b], Nmax), (q_pos[row] + 1) / m);
   int32_t* out = idx + (int64_t)row * k;
   const void* srow = BF16 ? (const void*)((const uint16_t*)scores + (int64_t)row * Nmax)
                           : (const void*)((const uint32_t*)scores + (int64_t)row * Nmax);
+  // ---- keys in registers: thread t owns entries [16 t, 16 t + 16).  Whole
+  // 16-byte loads leave before the row's visible count is known (their latency
+  // overlaps its loads); the keys are formed and masked after it
+  const int s0 = tid * 16;
+  const bool whole = vec && s0 + 16 <= Nmax;
+  u32x4 raw[BF16 ? 2 : 4];
+  if (whole) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(
+        BF16 ? (const void*)((const uint16_t*)srow + s0) : (const void*)((const uint32_t*)srow + s0));
+#pragma unroll
+    for (int j = 0; j < (BF16 ? 2 : 4); ++j) raw[j] = p[j];
+  }
+  const int nv = min(min(n_entries[b], Nmax), (q_pos[row] + 1) / m);
   if (nv <= k) {
     for (int i = tid; i < k; i += nt) out[i] = i < nv ? i : -1;
     return;
   }
-  // ---- keys in registers: thread t owns entries [16 t, 16 t + 16)
   uint32_t key[16];
-  const int s0 = tid * 16;
-  if (vec) {
-    // a wave whose 1,024 entries all lie past the visible count loads nothing
-    // (its keys are masked everywhere); in a causal prefill that is about half
-    if (__builtin_amdgcn_readfirstlane(tid >> 6) * 1024 < nv) {
-      load_keys16<BF16>(srow, s0, nv, Nmax, key);
-    } else {
+  if (whole) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) key[i] = 0u;
-    }
+    for (int j = 0; j < (BF16 ? 2 : 4); ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (BF16) {
+          key[8 * j + 2 * i] = bf16_key(raw[j][i] & 0xFFFFu);
+          key[8 * j + 2 * i + 1] = bf16_key(raw[j][i] >> 16);
+        } else {
+          key[4 * j + i] = f32_key(raw[j][i]);
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (s0 + i >= nv) key[i] = 0u;
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) key[i] = (s0 + i < nv) ? load_key<BF16>(srow, s0 + i) : 0u;
@@ -274,28 +308,32 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
       sh_above = remaining;
     }
   } else if (tid < 64) {
-    // ---- remaining digits over the candidates by wave 0 alone (no block barriers):
-    // fp32 keys 10 + 9 (W1 13) or 10 + 10 bits (W1 12), bf16 keys 6 bits (5..0)
+    // ---- remaining digits over the candidates by wave 0 alone (no block
+    // barriers), at most 6 bits each: one bin per lane, located by a prefix
+    // sum over the lanes (fp32 keys 20 or 19 bits in 4 digits, bf16 keys 6)
     uint32_t prefix = d1 << SH1, pmask = ~0u << SH1;
     int shift = SH1;
     while (shift > 0) {
-      const int width = BF16 ? 6 : min(shift, 10);
+      const int width = min(shift, 6);
       shift -= width;
       const int nbins = 1 << width;
       const uint32_t dmask = (uint32_t)nbins - 1u;
-      for (int i = lane; i < nbins; i += 64) hist[i] = 0;
+      hist[lane] = 0;
       __builtin_amdgcn_wave_barrier();
       for (int i = lane; i < nc; i += 64) {
         const uint32_t kk = cand[i];
         if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & dmask], 1);
       }
       __builtin_amdgcn_wave_barrier();
-      find_digit(hist, nbins, remaining, &sh_digit, &sh_above);
-      __builtin_amdgcn_wave_barrier();
-      const uint32_t dg = __shfl(sh_digit, 0);
-      remaining -= __shfl(sh_above, 0);
-      prefix |= dg << shift;
+      // lane j takes digit nbins - 1 - j: descending digits
+      const int c = lane < nbins ? hist[nbins - 1 - lane] : 0;
+      const int incl = wave_incl_sum(c);
+      const uint64_t hit = __ballot(incl - c < remaining && incl >= remaining);
+      const int j = (int)__builtin_ctzll(hit) & 63;
+      remaining -= __builtin_amdgcn_readlane(incl - c, j);
+      prefix |= (uint32_t)(nbins - 1 - j) << shift;
       pmask |= dmask << shift;
+      __builtin_amdgcn_wave_barrier();  // the bins are read before the next digit clears them
     }
     if (lane == 0) {
       sh_digit = prefix;
@@ -327,6 +365,25 @@ __global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ sco
     gt_before += g ? 1 : 0;
     eq_before += e ? 1 : 0;
   }
+}
+
+template <bool BF16, int W1>
+__global__ __launch_bounds__(1024) void topk_kernel(const void* __restrict__ scores,
+                                                    const int32_t* __restrict__ q_pos,
+                                                    const int32_t* __restrict__ n_entries, int Tq,
+                                                    int Nmax, int m, int k, int vec,
+                                                    int32_t* __restrict__ idx) {
+  topk_row<BF16, W1>(scores, q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
+}
+
+// many rows of fp32 scores (prefill): held to 64 registers so that four
+// 512-thread blocks reside per CU (measured: 32K prefill 389 -> 350 us; the
+// few-row kernel above stays unconstrained, which is faster for decode)
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8))) void topk_many_kernel(
+    const void* __restrict__ scores, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int Nmax, int m, int k, int vec,
+    int32_t* __restrict__ idx) {
+  topk_row<false, 12>(scores, q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
 }
 
 // ------------------------------------------------------------------ long rows
@@ -569,35 +626,6 @@ struct TkfSlice {
 
 static size_t tkf_hdr_bytes(int64_t slices) {
   return (size_t)((slices * (int64_t)sizeof(TkfSlice) + 255) / 256 * 256);
-}
-
-// Wave-wide helpers on DPP row moves (no LDS round trips); every lane of the
-// wave must be active.  DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] =
-// 0x4E, row_ror:n = 0x120 + n, row_shr:n = 0x110 + n.
-template <int CTRL>
-__device__ __forceinline__ int dpp_move(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
-}
-__device__ __forceinline__ int wave_all_max(int x) {
-  x = max(x, dpp_move<0xB1>(x));
-  x = max(x, dpp_move<0x4E>(x));
-  x = max(x, dpp_move<0x124>(x));
-  x = max(x, dpp_move<0x128>(x));  // every lane holds its row's maximum
-  const int a = max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16));
-  const int b = max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48));
-  return max(a, b);
-}
-__device__ __forceinline__ int wave_all_min(int x) { return -wave_all_max(-x); }
-// inclusive prefix sum over the lanes of the wave
-__device__ __forceinline__ int wave_incl_sum(int x) {
-  x += dpp_move<0x111>(x);
-  x += dpp_move<0x112>(x);
-  x += dpp_move<0x114>(x);
-  x += dpp_move<0x118>(x);  // prefix within each row of 16 lanes
-  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
-            r2 = __builtin_amdgcn_readlane(x, 47);
-  const int lane = threadIdx.x & 63;
-  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
 }
 
 // exclusive scan over the TKF_THREADS threads of a block with one barrier;
@@ -1014,8 +1042,8 @@ hipError_t launch_topk(const void* scores, csa_dtype score_t, const int32_t* q_p
     hipLaunchKernelGGL((topk_kernel<true, 13>), dim3(rows), dim3(threads), cand_bytes, s, scores,
                        q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
   else if (rows > 256)
-    hipLaunchKernelGGL((topk_kernel<false, 12>), dim3(rows), dim3(threads), cand_bytes, s, scores,
-                       q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
+    hipLaunchKernelGGL(topk_many_kernel, dim3(rows), dim3(threads), cand_bytes, s, scores, q_pos,
+                       n_entries, Tq, Nmax, m, k, vec, idx);
   else
     hipLaunchKernelGGL((topk_kernel<false, 13>), dim3(rows), dim3(threads), cand_bytes, s, scores,
                        q_pos, n_entries, Tq, Nmax, m, k, vec, idx);
