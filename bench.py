@@ -518,6 +518,51 @@ def run_prefill(args, torch, I, G):
     return res, inp
 
 
+# ------------------------------------------------------------------ compression
+def compress_flops(sp, T):
+    """Algorithmic flops of the prefill compressor: the projections (main KV
+    2 or 4, index keys 4, window rows 1) of every token, 2 flops per MAC."""
+    nkv = 4 if sp.m == 4 else 2
+    f = nkv * T * sp.c * sp.d * 2 + T * sp.c * sp.d * 2
+    if sp.nI:
+        f += 4 * T * sp.cI * sp.d * 2
+    return f
+
+
+def run_compress(args, torch, I, G):
+    """The prefill workload's compression alone (csa_compress for the main KV
+    entries, the index keys and the per-token window rows): not part of the
+    prefill metric, measured as its own row."""
+    sp = I.CONFIGS["prefill_32k"]
+    dev = torch.device("cuda", 0)
+    inp = I.prefill_inputs(sp)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        p = G.upload_prefill(inp, dev)
+        for _ in range(max(args.warmup, 1)):
+            G.prefill_compress(p, stream)
+    torch.cuda.synchronize()
+    elapsed, step_us = timed_steps(torch, stream, lambda i: G.prefill_compress(p, stream), args.steps)
+    fl = compress_flops(sp, sp.T)
+    dist = distribution(step_us)
+    tf = fl / (dist["median"] * 1e-6) / 1e12
+    ms = elapsed / args.steps * 1e3
+    return dict(
+        metric=METRIC, value=fl / (ms * 1e-3) / 1e12, unit="TFLOP/s", n_gpus=1, steps=args.steps,
+        warmup=args.warmup, ms_per_step=ms, higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16", data="synthetic",
+        config=dict(workload="compress_32k", seq_len=sp.T, hidden=sp.d, m=sp.m, head_dim=sp.c,
+                    indexer_dim=sp.cI, calls="main KV (4 projections), index keys (4), window (1)"),
+        roofline=dict(bound="mfma", kernel="csa_compress (3 calls: weight transposes, "
+                      "oproj_big_kernel, pool_kernel)", achieved=tf, peak=BF16_PEAK_TFLOPS,
+                      unit="TFLOP/s", frac=tf / BF16_PEAK_TFLOPS, traffic=None,
+                      algorithmic_flops_per_launch=fl, avg_launch_us=dist["median"],
+                      timing="HIP events at the step boundaries (median step)"),
+        step=dict(step_us=dist),
+        cpu_baseline=None,
+    )
+
+
 # ------------------------------------------------------------------ tiny configurations
 def run_tiny(args, torch, I, G):
     """Tiny CSA / HCA: one sequence of 1024 tokens, hidden 256, fp32.  A step is
@@ -593,7 +638,7 @@ def main():
     ap.add_argument("--config", default="decode_64k",
                     choices=["decode_64k", "hca_decode_1m", "decode_1m_fp4", "prefill_32k",
                              "prefill_32k_mxfp4", "oproj_decode", "oproj_prefill", "tiny_csa",
-                             "tiny_hca"])
+                             "tiny_hca", "compress_32k"])
     ap.add_argument("--copies", type=int, default=6, help="cache copies rotated (cold cache)")
     ap.add_argument("--graph", action="store_true", help="decode: replay each step as a HIP graph")
     ap.add_argument("--chunks", type=int, default=1,
@@ -617,6 +662,9 @@ def main():
     from long_context_sparse_10_amd import pipeline as G
     if args.config.startswith("tiny"):
         print(json.dumps(run_tiny(args, torch, I, G)), flush=True)
+        return
+    if args.config == "compress_32k":
+        print(json.dumps(run_compress(args, torch, I, G)), flush=True)
         return
     if args.config in OPROJ:
         res, case = run_oproj(args, torch)

@@ -139,7 +139,9 @@ csa_status csa_prep_rows(const void* x, csa_dtype x_t, int64_t rows, int c,
  *  norm_w  [c] fp32 or NULL (no RMSNorm; index keys use NULL and rope_dims 0).
  *  out     [B, T / m, row bytes of out_t] (+ out_scale [B, T/m, c/32] for MXFP4).
  *          Tokens beyond the last complete block are not compressed.
- *  ws      fp32 projection scratch (see the workspace protocol above).
+ *  ws      fp32 projection scratch (see the workspace protocol above); with bf16
+ *          H, d a multiple of 64 and B * T >= 256 it also holds the projection
+ *          weights transposed to [c, d] (bf16).
  */
 csa_status csa_compress(const void* H, csa_dtype h_t, int B, int T, int d,
                         const void* W_kv_a, const void* W_z_a,

@@ -158,13 +158,30 @@ static csa_status compress_impl(const void* H, csa_dtype h_t, int B, int T, int 
   if (!overlap && (W_kv_b != nullptr || W_z_b != nullptr)) return CSA_ERR_INVALID;
   const int nproj = single ? 1 : (overlap ? 4 : 2);
   const size_t slot = (size_t)B * T * c;
-  if (ws_query(ws, ws_bytes, slot * nproj * sizeof(float), &st)) return st;
-  float* P = (float*)ws;
   const int M = B * T;
+  // many tokens of bf16: the projections' weights transposed to [c, d] in the
+  // workspace, then one grouped launch of the 256 x 256-tile product
+  const bool tiled = h_t == CSA_BF16 && d % 64 == 0 && M >= 256 && c >= 16 &&
+                     (uintptr_t)H % 16 == 0;
+  const size_t p_bytes = (slot * nproj * sizeof(float) + 255) / 256 * 256;
+  const size_t wt_bytes = tiled ? (size_t)nproj * c * d * sizeof(uint16_t) : 0;
+  if (ws_query(ws, ws_bytes, p_bytes + wt_bytes, &st)) return st;
+  float* P = (float*)ws;
   const void* Ws[4] = {W_kv_a, W_z_a, W_kv_b, W_z_b};
-  for (int i = 0; i < nproj; ++i) {
-    const hipError_t e = launch_gemm(H, Ws[i], h_t, P + i * slot, M, c, d, stream);
-    if (e != hipSuccess) return CSA_ERR_LAUNCH;
+  if (tiled) {
+    uint16_t* WT = reinterpret_cast<uint16_t*>((char*)ws + p_bytes);
+    for (int i = 0; i < nproj; ++i)
+      if (launch_transpose_bf16((const uint16_t*)Ws[i], WT + (size_t)i * c * d, d, c, stream) !=
+          hipSuccess)
+        return CSA_ERR_LAUNCH;
+    if (launch_gemm_nt((const uint16_t*)H, d, WT, (int64_t)c * d, P, c, (int64_t)slot, M, c, d,
+                       nproj, stream) != hipSuccess)
+      return CSA_ERR_LAUNCH;
+  } else {
+    for (int i = 0; i < nproj; ++i) {
+      const hipError_t e = launch_gemm(H, Ws[i], h_t, P + i * slot, M, c, d, stream);
+      if (e != hipSuccess) return CSA_ERR_LAUNCH;
+    }
   }
   return launch_status(launch_pool(P, single ? nullptr : P + slot, overlap ? P + 2 * slot : nullptr,
                                    overlap ? P + 3 * slot : nullptr, bias_a, bias_b, B, T, m, c,

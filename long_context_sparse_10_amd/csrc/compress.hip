@@ -190,6 +190,31 @@ __global__ __launch_bounds__(256) void gemm_bf16_mfma_kernel(const uint16_t* __r
     }
 }
 
+// dst[c][r] = src[r][c] for a [R, Cc] bf16 matrix (weights [d, c] -> [c, d]),
+// through a 32 x 33 shared tile
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             uint16_t* __restrict__ dst, int R,
+                                                             int Cc) {
+  __shared__ uint16_t t[32][33];
+  const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int j = ty; j < 32; j += 8) {
+    const int r = r0 + j, c = c0 + tx;
+    t[j][tx] = (r < R && c < Cc) ? src[(int64_t)r * Cc + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int j = ty; j < 32; j += 8) {
+    const int c = c0 + j, r = r0 + tx;
+    if (c < Cc && r < R) dst[(int64_t)c * R + r] = t[tx][j];
+  }
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int R, int Cc, hipStream_t s) {
+  dim3 grid((Cc + 31) / 32, (R + 31) / 32);
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, dst, R, Cc);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const void* A, const void* Bm, csa_dtype t, float* C, int M, int N, int K,
                        hipStream_t s) {
   if (t == CSA_BF16 && K % GB_K == 0 && N % 8 == 0) {

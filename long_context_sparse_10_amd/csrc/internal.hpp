@@ -42,6 +42,13 @@ hipError_t launch_prep_rows(const void* x, csa_dtype x_t, int64_t rows, int c,
 // C[M, N] (fp32) = A[M, K] * B[K, N]; A and B both f32 or both bf16, row-major
 hipError_t launch_gemm(const void* A, const void* Bm, csa_dtype t, float* C, int M, int N, int K,
                        hipStream_t s);
+// dst[c][r] = src[r][c], bf16 [R, Cc] -> [Cc, R]
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int R, int Cc, hipStream_t s);
+// oproj.hip: C_g[M, N] (fp32, row stride ldc, groups c_goff apart) = A[M, K] . W_g[N, K]^T,
+// W_g = W + g * w_gstride (bf16, K % 64 == 0, 16-byte aligned rows)
+hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t w_gstride,
+                          float* C, int64_t ldc, int64_t c_goff, int M, int N, int K, int groups,
+                          hipStream_t s);
 
 hipError_t launch_pool(const float* Ca, const float* Za, const float* Cb, const float* Zb,
                        const float* bias_a, const float* bias_b, int B, int T, int m, int c,

@@ -367,6 +367,20 @@ static bool skinny_fits(int M, int N, int K) {
   return M <= 64 && N % OS_COLS == 0 && K % ks == 0 && K / ks <= OS_MAX_SPLITS;
 }
 
+// C_g[M, N] (fp32, row stride ldc, groups c_goff apart) = A[M, K] . W_g[N, K]^T
+// with W_g = W + g * w_gstride, for g < groups, on the 256 x 256-tile kernel
+// (the compressor's projections: M = tokens, K = d).  K % 64 == 0 and 16-byte
+// aligned rows are the caller's to check.
+hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* W, int64_t w_gstride,
+                          float* C, int64_t ldc, int64_t c_goff, int M, int N, int K, int groups,
+                          hipStream_t s) {
+  const int64_t nN = (N + OB_N - 1) / OB_N, nM = (M + OB_M - 1) / OB_M;
+  dim3 grid((unsigned)((nM + 7) / 8 * 8 * nN * groups));
+  hipLaunchKernelGGL(oproj_big_kernel, grid, dim3(256), 0, s, A, lda, (int64_t)0, W, w_gstride,
+                     (void*)C, ldc, c_goff, 0, M, N, K);
+  return hipGetLastError();
+}
+
 // one product C[M, groups * N] = A . W^T over `groups` column groups (C row
 // stride ldc = groups * N); `part` is fp32 workspace for the skinny path
 static hipError_t launch_oproj_gemm(const void* A, int64_t lda, int64_t a_goff, const void* W,
