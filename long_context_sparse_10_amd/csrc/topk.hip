@@ -613,11 +613,13 @@ __global__ __launch_bounds__(TKM_THREADS) void topk_emit_kernel(
 // Rows run in groups of at most TKF_MAX_SLICES / P (P slices per row) per
 // launch pair, which bounds the workspace: per slice a 16-byte header and a
 // 128 KB histogram addressed by key (only [lo, hi] is written and read).
-constexpr int TKF_THREADS = 1024;
+constexpr int TKF_THREADS = 512;
 constexpr int TKF_SLICE = 16 * TKF_THREADS;   // entries per slice block
 constexpr int TKF_KEYS = 1 << 16;             // bf16 keys
 constexpr int TKF_MAX_SLICES = 1024;          // slices per launch pair
-static_assert(TKF_KEYS / 64 == TKF_THREADS, "one 64-key group per thread");
+constexpr int TKF_NW = TKF_THREADS / 64;      // waves per block
+constexpr int TKF_GPT = TKF_KEYS / 64 / TKF_THREADS;  // 64-key groups per thread
+static_assert(TKF_GPT * TKF_THREADS * 64 == TKF_KEYS && TKF_NW <= 16, "block shape");
 static_assert(TKF_MAX_SLICES % TKF_THREADS == 0, "whole header rounds");
 
 struct TkfSlice {
@@ -767,8 +769,8 @@ __global__ __launch_bounds__(TKF_THREADS) void topk_fine_hist_kernel(
 #pragma unroll
   for (int i = 0; i < 16; ++i)
     if (s0 + i < nv) atomicAdd(&h[key[i] >> 1], 1u << ((key[i] & 1u) << 4));
-  const int hi = wave_all_max(red[0][lane & 15]);
-  int lo = wave_all_min(red[1][lane & 15]);
+  const int hi = wave_all_max(lane < TKF_NW ? red[0][lane] : -1);
+  int lo = wave_all_min(lane < TKF_NW ? red[1][lane] : TKF_KEYS);
   const int w_hi = hi >> 1;
   __syncthreads();  // histogram complete
   if (cs >= k) {
@@ -789,9 +791,15 @@ __global__ __launch_bounds__(TKF_THREADS) void topk_fine_hist_kernel(
         if (lane == 0) sh_lo = 64 * gs + 63 - (int)__builtin_ctzll(hit2);
       }
     } else {
-      // thread t counts group g_hi - t (the range spans at most 1024 groups)
-      const int g = g_hi - tid;
-      const int cnt = g >= g_lo ? tkf_group_count(h, g, tid) : 0;
+      // thread t counts groups g_hi - TKF_GPT t - j, j < TKF_GPT (descending;
+      // the range spans at most 1024 groups)
+      int gc[TKF_GPT], cnt = 0;
+#pragma unroll
+      for (int j = 0; j < TKF_GPT; ++j) {
+        const int g = g_hi - TKF_GPT * tid - j;
+        gc[j] = g >= g_lo ? tkf_group_count(h, g, tid + j) : 0;
+        cnt += gc[j];
+      }
       if (tid == 0) {
         sh_grp[0] = g_lo;
         sh_grp[1] = 0;
@@ -799,8 +807,10 @@ __global__ __launch_bounds__(TKF_THREADS) void topk_fine_hist_kernel(
       int total;
       const int excl = tkf_block_excl(cnt, scan_ws, &total);
       if (excl < k && excl + cnt >= k) {
-        sh_grp[0] = g;
-        sh_grp[1] = excl;
+        int acc = excl, j = 0;
+        while (j + 1 < TKF_GPT && acc + gc[j] < k) acc += gc[j++];
+        sh_grp[0] = g_hi - TKF_GPT * tid - j;
+        sh_grp[1] = acc;
       }
       __syncthreads();
       if (tid < 64) {
@@ -871,8 +881,8 @@ __global__ __launch_bounds__(TKF_THREADS) void topk_fine_emit_kernel(
   }
   if (tid < 4) res[tid] = tid == 0 ? -1 : 0;
   __syncthreads();
-  L = wave_all_max(red[0][lane & 15]);
-  H = wave_all_max(red[1][lane & 15]);
+  L = wave_all_max(lane < TKF_NW ? red[0][lane] : -1);
+  H = wave_all_max(lane < TKF_NW ? red[1][lane] : -1);
   // rank k from the top: thread t takes key top - t; counts of all slices (c)
   // and of the slices before this one (cb)
   const uint16_t* hrow = hist + (int64_t)lr * P * TKF_KEYS;
@@ -881,22 +891,22 @@ __global__ __launch_bounds__(TKF_THREADS) void topk_fine_emit_kernel(
     const int kx = top - tid;
     int c = 0, cb = 0;
     if (kx >= L) {
-      for (int sb = 0; sb < pv; sb += 16) {
+      for (int sb = 0; sb < pv; sb += 32) {
         // unconditional loads from stored bins (slice and key clamped into a
-        // stored range), masked afterwards: all 16 are in flight at once
-        uint32_t v[16];
-        bool in[16];
+        // stored range), masked afterwards: all 32 are in flight at once
+        uint32_t v[32];
+        bool in[32];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 32; ++j) {
           const int sl = min(sb + j, pv - 1);
           const int lo = sh[sl].lo, hi = sh[sl].hi;
           in[j] = sb + j < pv && kx >= lo && kx <= hi;
           v[j] = hrow[(int64_t)sl * TKF_KEYS + min(max(kx, lo), hi)];
         }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = in[j] ? v[j] : 0u;
+        for (int j = 0; j < 32; ++j) v[j] = in[j] ? v[j] : 0u;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 32; ++j) {
           c += (int)v[j];
           cb += sb + j < p ? (int)v[j] : 0;
         }
