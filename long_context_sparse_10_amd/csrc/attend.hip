@@ -979,17 +979,42 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, Rope 
                                                     nrows * nsplit * nh * c) +
                      (int64_t)row * nsplit * nh * 2;
   const float z = a.sink[h];
-  float M = z;
+  float M = z, den, o0 = 0.f, o1 = 0.f;
+  if (nsplit <= 16) {
+    // every split's (m, l) and partial requested at once, then merged in
+    // split order (the same arithmetic as the general loop below)
+    float2 ml[16];
+    uint32_t v[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < nsplit) {
+        ml[s] = *reinterpret_cast<const float2*>(wml + ((int64_t)s * nh + h) * 2);
+        v[s] = *reinterpret_cast<const uint32_t*>(wo + ((int64_t)s * nh + h) * c + d);
+      }
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < nsplit) M = fmaxf(M, ml[s].x);
+    den = __expf(z - M);
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s < nsplit) {
+        const float wgt = ml[s].y * __expf(ml[s].x - M);
+        den += wgt;
+        o0 = fmaf(__uint_as_float(v[s] << 16), wgt, o0);
+        o1 = fmaf(__uint_as_float(v[s] & 0xFFFF0000u), wgt, o1);
+      }
+  } else {
 #pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wml[((int64_t)s * nh + h) * 2]);
-  float den = __expf(z - M), o0 = 0.f, o1 = 0.f;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wml[((int64_t)s * nh + h) * 2]);
+    den = __expf(z - M);
 #pragma unroll 8
-  for (int s = 0; s < nsplit; ++s) {
-    const float wgt = wml[((int64_t)s * nh + h) * 2 + 1] * __expf(wml[((int64_t)s * nh + h) * 2] - M);
-    den += wgt;
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(wo + ((int64_t)s * nh + h) * c + d);
-    o0 = fmaf(__uint_as_float(v << 16), wgt, o0);
-    o1 = fmaf(__uint_as_float(v & 0xFFFF0000u), wgt, o1);
+    for (int s = 0; s < nsplit; ++s) {
+      const float wgt = wml[((int64_t)s * nh + h) * 2 + 1] * __expf(wml[((int64_t)s * nh + h) * 2] - M);
+      den += wgt;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(wo + ((int64_t)s * nh + h) * c + d);
+      o0 = fmaf(__uint_as_float(v << 16), wgt, o0);
+      o1 = fmaf(__uint_as_float(v & 0xFFFF0000u), wgt, o1);
+    }
   }
   const float inv = 1.0f / den;
   o0 *= inv;
@@ -1028,11 +1053,13 @@ static void plan_splits(const AttendArgs& a, int* chunk, int* nsplit) {
     *nsplit = 1;
     return;
   }
-  // 8 splits up to 4096 slots, 16 beyond: a decode batch of 16-32 rows then
-  // gives one block per compute unit
-  const int want = total <= 4096 ? 8 : 16;
+  // 8 splits per 64-head group up to 4096 slots (at most 16), 16 beyond: a
+  // decode batch of 8 rows x 128 heads or 32 rows x 64 heads then gives about
+  // one block per compute unit.  Splits are whole tiles, at least 3.
+  const int hgroups = a.nh / 64;
+  const int want = total <= 4096 ? (hgroups > 1 ? 16 : 8) : 16;
   int ch = ((total + want - 1) / want + AT_TILE - 1) / AT_TILE * AT_TILE;
-  ch = ch < 4 * AT_TILE ? 4 * AT_TILE : (ch > AT_TAB ? AT_TAB : ch);
+  ch = ch < 3 * AT_TILE ? 3 * AT_TILE : (ch > AT_TAB ? AT_TAB : ch);
   *chunk = ch;
   *nsplit = (total + ch - 1) / ch;
 }
