@@ -102,18 +102,27 @@ def prefill_flops(sp, T):
 
 # ------------------------------------------------------------------ timing helpers
 def timed_steps(torch, stream, run_step, steps):
-    """K steps back to back on `stream`, one HIP event at each step boundary:
-    (wall seconds, per-step GPU microseconds)."""
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    """K steps back to back on `stream`, bracketed by a synchronize on both
+    sides and nothing between the steps: wall seconds (the value).  Then K
+    more with a HIP event at each step boundary: per-step GPU microseconds
+    (the distribution; each event adds its own dispatch gap, a few us).
+    Also the host seconds spent launching the K steps of the first pass."""
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(steps):
+            run_step(i)
+    host = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     with torch.cuda.stream(stream):
         ev[0].record(stream)
         for i in range(steps):
             run_step(i)
             ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall, np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)])
+    return wall, np.array([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]), host
 
 
 def stage_times(torch, stream, stages, reps):
@@ -309,7 +318,7 @@ def run_decode(args, torch, I, G):
             run_step(i)
     torch.cuda.synchronize()
     # the timed steps (value, and the distribution of the step)
-    elapsed, step_us = timed_steps(torch, stream, run_step, args.steps)
+    elapsed, step_us, host_s = timed_steps(torch, stream, run_step, args.steps)
     # per-call times: each call back to back over the rotated copies
     stages = [(kind, (lambda i, k=kind: call[k](copies[i % len(copies)], stream)))
               for kind in kinds]
@@ -353,7 +362,8 @@ def run_decode(args, torch, I, G):
                              "rotated copies, on its launch stream, after the timed steps"),
         roofline_step=dict(bound="hbm", achieved=step_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                            frac=step_gbs / HBM_PEAK_GBS, algorithmic_bytes=step_bytes,
-                           step_us=dist, copy_gbs=round(copy_gbs, 1),
+                           step_us=dist, host_launch_us=round(host_s / args.steps * 1e6, 2),
+                           copy_gbs=round(copy_gbs, 1),
                            frac_of_copy=step_gbs / copy_gbs, kernels=per,
                            launch=("HIP graph per cache copy" if args.graph else "eager launches")
                            + (f"; batch in {args.chunks} groups on 2 streams"
@@ -473,7 +483,7 @@ def run_prefill(args, torch, I, G):
     import long_context_sparse_10_amd as L
     sfmt = L.BF16 if sp.index_format == "mxfp4" else L.F32
     scale = 1.0 / math.sqrt(sp.c)
-    elapsed, step_us = timed_steps(torch, stream, lambda i: G.prefill_attention_path(p, stream),
+    elapsed, step_us, host_s = timed_steps(torch, stream, lambda i: G.prefill_attention_path(p, stream),
                                    args.steps)
     stages = [
         ("indexer", lambda i: G.prefill_indexer(p, stream)),
@@ -542,7 +552,7 @@ def run_compress(args, torch, I, G):
         for _ in range(max(args.warmup, 1)):
             G.prefill_compress(p, stream)
     torch.cuda.synchronize()
-    elapsed, step_us = timed_steps(torch, stream, lambda i: G.prefill_compress(p, stream), args.steps)
+    elapsed, step_us, host_s = timed_steps(torch, stream, lambda i: G.prefill_compress(p, stream), args.steps)
     fl = compress_flops(sp, sp.T)
     dist = distribution(step_us)
     tf = fl / (dist["median"] * 1e-6) / 1e12
@@ -583,7 +593,7 @@ def run_tiny(args, torch, I, G):
         for i in range(max(args.warmup, 1)):
             step(i)
     torch.cuda.synchronize()
-    elapsed, step_us = timed_steps(torch, stream, step, args.steps)
+    elapsed, step_us, host_s = timed_steps(torch, stream, step, args.steps)
     stages = [("compress", lambda i: G.prefill_compress(p, stream)),
               ("attention_path", lambda i: G.prefill_attention_path(p, stream))]
     avg = stage_times(torch, stream, stages, args.steps)
