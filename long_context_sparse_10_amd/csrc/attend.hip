@@ -1035,11 +1035,15 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a, Rope 
 }
 
 // ============================================================ dispatch
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 static bool use_mfma(const AttendArgs& a) {
-  // FP8 rows are staged as 448 e4m3 + 64 bf16 bytes: RoPE on the last 64
+  // FP8 rows are staged as 448 e4m3 + 64 bf16 bytes: RoPE on the last 64.
+  // Queries, rows and outputs move in 16-byte pieces.
   return a.c == AT_C && a.nh % 64 == 0 && (a.kv_t == CSA_BF16 || a.kv_t == CSA_FP8MIX) &&
          (a.q_t == CSA_BF16 || a.q_t == CSA_F32) && a.rope_dims % 2 == 0 && a.rope_dims <= AT_C &&
-         (a.kv_t != CSA_FP8MIX || a.rope_dims == 64);
+         (a.kv_t != CSA_FP8MIX || a.rope_dims == 64) && aligned16(a.q) && aligned16(a.kv) &&
+         aligned16(a.win) && aligned16(a.out);
 }
 
 // slot split: a function of the per-row slot count only (never of the batch

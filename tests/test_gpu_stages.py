@@ -517,6 +517,23 @@ def test_attend_window_edges_and_empty_selection():
         check_decode_attention("attend window edges", g, inp, b, idx[b], out[b, 0], b=b)
 
 
+def test_attend_unaligned_output_takes_generic_kernel():
+    """An output pointer off 16-byte alignment cannot take the matrix-core
+    kernels (their stores are 16 bytes wide): the call falls back to the
+    generic kernel and still matches the oracle."""
+    d = dev()
+    sp, inp, idx = _attend_case("decode_64k", [4100, 300], 330)
+    g = G.upload_decode(inp, d)
+    buf = torch.zeros(g.out.numel() + 8, dtype=g.out.dtype, device=d)
+    g.out = buf[1:1 + g.out.numel()].view(g.out.shape)    # 2 bytes past a 16-byte boundary
+    assert g.out.data_ptr() % 16 == 2
+    G.decode_attend(g, idx=torch.from_numpy(idx).reshape(sp.B, 1, sp.k).to(d))
+    torch.cuda.synchronize()
+    out = np64(g.out)
+    for b in range(sp.B):
+        check_decode_attention("attend unaligned out", g, inp, b, idx[b], out[b, 0], b=b)
+
+
 def test_attend_deterministic_and_batch_invariant():
     d = dev()
     sp, inp, idx = _attend_case("decode_64k", [4100, 9000, 300], 320)
