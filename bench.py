@@ -45,13 +45,13 @@ METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP
 # of known size (--copy-probe).  An entry holds for the kernel source it was
 # taken on (sha256 of the .hip file); after any change it reports null.
 TRAFFIC = {
-    'decode_64k': {"kernel": "indexer_mfma_kernel", "src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 67722.5, "write_kib": 2048.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'decode_64k': {"kernel": "indexer_mfma_kernel", "src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 67723.0, "write_kib": 2048.0, "fetch_scale": 1.9998, "write_scale": 1.0},
     'decode_1m_fp4': {"kernel": "indexer_mfma_kernel", "src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 69941.3, "write_kib": 4096.0, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'prefill_32k': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "0a23d22aaf61bfe2546234d737ead92c3f47c3a3d8c5ed83d34d453e4f1d089e", "fetch_kib": 3583463.5, "write_kib": 2097152.0, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'prefill_32k_mxfp4': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "0a23d22aaf61bfe2546234d737ead92c3f47c3a3d8c5ed83d34d453e4f1d089e", "fetch_kib": 3607497.1, "write_kib": 2097152.0, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'oproj_decode': {"kernel": "grouped_out_proj", "src": "oproj.hip", "sha256": "99d8386e33f20e6b4550c52e1cad5985505842be7148f54ce0c4b5e890c9f760", "fetch_kib": 80948.4, "write_kib": 8967.4, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'oproj_prefill': {"kernel": "grouped_out_proj", "src": "oproj.hip", "sha256": "99d8386e33f20e6b4550c52e1cad5985505842be7148f54ce0c4b5e890c9f760", "fetch_kib": 4553178.6, "write_kib": 842469.5, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'hca_decode_1m': {"kernel": "attend_mfma_kernel + attend_combine_kernel", "src": "attend.hip", "sha256": "0a23d22aaf61bfe2546234d737ead92c3f47c3a3d8c5ed83d34d453e4f1d089e", "fetch_kib": 75736.5, "write_kib": 17536.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'prefill_32k': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "053c38122d5216c8451cc9f17bdafa5255d98a3c1f42a277ee78d72159d98d1b", "fetch_kib": 3497874.8, "write_kib": 2097152.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'prefill_32k_mxfp4': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "053c38122d5216c8451cc9f17bdafa5255d98a3c1f42a277ee78d72159d98d1b", "fetch_kib": 3507654.9, "write_kib": 2097152.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'oproj_decode': {"kernel": "grouped_out_proj", "src": "oproj.hip", "sha256": "fdf6181d79947eb13a3532a65336dabd0336924f79cbadcfe230d06ce9d3d945", "fetch_kib": 80943.6, "write_kib": 8968.2, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'oproj_prefill': {"kernel": "grouped_out_proj", "src": "oproj.hip", "sha256": "fdf6181d79947eb13a3532a65336dabd0336924f79cbadcfe230d06ce9d3d945", "fetch_kib": 4495578.3, "write_kib": 842334.2, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'hca_decode_1m': {"kernel": "attend_mfma_kernel + attend_combine_kernel", "src": "attend.hip", "sha256": "053c38122d5216c8451cc9f17bdafa5255d98a3c1f42a277ee78d72159d98d1b", "fetch_kib": 75753.1, "write_kib": 17536.0, "fetch_scale": 1.9998, "write_scale": 1.0},
 }
 
 
