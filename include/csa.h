@@ -402,8 +402,8 @@ csa_status hca_attend_paged(const void* q, csa_dtype q_t, const float* q_norm_w,
  *  go to a scratch array of CSA_NOALLOC_SCRATCH_BYTES inside the library's
  *  device memory, one copy per GPU, held until the process ends.  A call whose
  *  partials need more returns CSA_ERR_WORKSPACE and launches nothing (32 MiB
- *  covers, e.g., 32 decode rows x 64 heads or 8 x 128 heads at k = 1024 and a
- *  128-row window, 8 splits).
+ *  covers, e.g., 32 decode rows x 64 heads in 8 splits or 8 x 128 heads in 12
+ *  splits, at k = 1024 and a 128-row window).
  *  Every call looks up the current device's scratch address the first time
  *  it runs on that device (CSA_ERR_LAUNCH if the lookup fails); an empty call
  *  (B == 0) does only that, e.g. before a graph capture.
