@@ -458,7 +458,7 @@ __device__ __forceinline__ void attend_store_out(const AttendArgs& a, int row, i
 //    registers, up to two tiles ahead of the one being committed, and commits
 //    them (expanding e4m3 to bf16) to the LDS tile the math waves are not using.
 // One barrier per tile separates the two buffers.
-template <int KVF, bool QBF16>
+template <int KVF, bool QBF16, int RING>
 __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt, int chunk,
                                                          int nsplit, void* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) AttendSmem sm;
@@ -670,6 +670,48 @@ __global__ __launch_bounds__(512) void attend_mfma_kernel(AttendArgs a, Rope rt,
   const int tr_c = 4 * (li & 3);
 
 
+  if (!math && RING == 3) {
+    // ---- loaders, long split lists: a ring of 3 register sets; tile u lives
+    // in set u % 3 and phase u stages tile u + 3, so three tiles are in
+    // flight per block while one is committed.  Same barrier count as below.
+    u32x4 st0[8], st1[8], st2[8];
+    uint32_t ok0 = 0u, ok1 = 0u, ok2 = 0u;
+    if (ntiles > 0) {
+      CSA_STAGE(st0, ok0, 0);
+      CSA_STAGE(st1, ok1, 1);
+      CSA_STAGE(st2, ok2, 2);
+      CSA_COMMIT(st0, ok0, 0);
+      CSA_STAGE(st0, ok0, 3);
+    }
+    __syncthreads();
+#define CSA_PHASE3(STG, OK, U)                                                               \
+    {                                                                                        \
+      CSA_COMMIT(STG, OK, (U) & 1);                                                          \
+      CSA_STAGE(STG, OK, (U) + 3);                                                           \
+      __syncthreads();                                                                       \
+    }
+#define CSA_LAST_PHASE3(STG, OK, U)                                                          \
+    if ((U) <= ntiles) {                                                                     \
+      if ((U) < ntiles) CSA_COMMIT(STG, OK, (U) & 1);                                        \
+      if ((U) + 3 < ntiles) CSA_STAGE(STG, OK, (U) + 3);                                     \
+      __syncthreads();                                                                       \
+    }
+    int u = 1;
+    for (; u + 5 < ntiles; u += 3) {
+      CSA_PHASE3(st1, ok1, u);
+      CSA_PHASE3(st2, ok2, u + 1);
+      CSA_PHASE3(st0, ok0, u + 2);
+    }
+    CSA_LAST_PHASE3(st1, ok1, u);
+    CSA_LAST_PHASE3(st2, ok2, u + 1);
+    CSA_LAST_PHASE3(st0, ok0, u + 2);
+    CSA_LAST_PHASE3(st1, ok1, u + 3);
+    CSA_LAST_PHASE3(st2, ok2, u + 4);
+    CSA_LAST_PHASE3(st0, ok0, u + 5);
+#undef CSA_PHASE3
+#undef CSA_LAST_PHASE3
+    return;
+  }
   if (!math) {
     // ---- loaders: a ring of 2 register sets; tile u lives in set u % 2.
     // While the math waves compute tile t from X[t & 1], tile t+1 is committed
@@ -1110,14 +1152,17 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t s) {
   dim3 grid((unsigned)((int64_t)nsplit * (a.nh / 64) * rows8));
   void* w = ws;
   const bool qb = a.q_t == CSA_BF16;
-  if (a.kv_t == CSA_BF16 && qb)
-    hipLaunchKernelGGL((attend_mfma_kernel<CSA_BF16, true>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+  // splits of 8 tiles or more (long dense lists) keep three tiles in flight
+  if (a.kv_t == CSA_BF16 && qb && chunk >= 8 * AT_TILE)
+    hipLaunchKernelGGL((attend_mfma_kernel<CSA_BF16, true, 3>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+  else if (a.kv_t == CSA_BF16 && qb)
+    hipLaunchKernelGGL((attend_mfma_kernel<CSA_BF16, true, 2>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   else if (a.kv_t == CSA_BF16)
-    hipLaunchKernelGGL((attend_mfma_kernel<CSA_BF16, false>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+    hipLaunchKernelGGL((attend_mfma_kernel<CSA_BF16, false, 2>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   else if (qb)
-    hipLaunchKernelGGL((attend_mfma_kernel<CSA_FP8MIX, true>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+    hipLaunchKernelGGL((attend_mfma_kernel<CSA_FP8MIX, true, 2>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   else
-    hipLaunchKernelGGL((attend_mfma_kernel<CSA_FP8MIX, false>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
+    hipLaunchKernelGGL((attend_mfma_kernel<CSA_FP8MIX, false, 2>), grid, dim3(512), 0, s, a, rt, chunk, nsplit, w);
   if (nsplit > 1)
     hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)(rows8 * a.nh)),
                        dim3((a.c / 2 + 63) / 64 * 64), 0, s, a, rt, nsplit, (const void*)w);
