@@ -47,11 +47,11 @@ METRIC = "CSA decode query-tokens/s @64K–1M ctx, % HBM roofline; prefill TFLOP
 TRAFFIC = {
     'decode_64k': {"kernel": "indexer_mfma_kernel", "src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 67723.0, "write_kib": 2048.0, "fetch_scale": 1.9998, "write_scale": 1.0},
     'decode_1m_fp4': {"kernel": "indexer_mfma_kernel", "src": "indexer.hip", "sha256": "11edc41b8d401743b8505978f26a4f4bd07674f12674e731507cd4bd8cfe797c", "fetch_kib": 69941.3, "write_kib": 4096.0, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'prefill_32k': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "053c38122d5216c8451cc9f17bdafa5255d98a3c1f42a277ee78d72159d98d1b", "fetch_kib": 3497874.8, "write_kib": 2097152.0, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'prefill_32k_mxfp4': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "053c38122d5216c8451cc9f17bdafa5255d98a3c1f42a277ee78d72159d98d1b", "fetch_kib": 3507654.9, "write_kib": 2097152.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'prefill_32k': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "7ecf3628d32825a140dc0e8963b807f6116a1d2a6f0b1f10e08a7e180c5977b0", "fetch_kib": 3585243.6, "write_kib": 2097152.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'prefill_32k_mxfp4': {"kernel": "attend_pf_kernel", "src": "attend.hip", "sha256": "7ecf3628d32825a140dc0e8963b807f6116a1d2a6f0b1f10e08a7e180c5977b0", "fetch_kib": 3528917.9, "write_kib": 2097152.0, "fetch_scale": 1.9998, "write_scale": 1.0},
     'oproj_decode': {"kernel": "grouped_out_proj", "src": "oproj.hip", "sha256": "fdf6181d79947eb13a3532a65336dabd0336924f79cbadcfe230d06ce9d3d945", "fetch_kib": 80943.6, "write_kib": 8968.2, "fetch_scale": 1.9998, "write_scale": 1.0},
     'oproj_prefill': {"kernel": "grouped_out_proj", "src": "oproj.hip", "sha256": "fdf6181d79947eb13a3532a65336dabd0336924f79cbadcfe230d06ce9d3d945", "fetch_kib": 4495578.3, "write_kib": 842334.2, "fetch_scale": 1.9998, "write_scale": 1.0},
-    'hca_decode_1m': {"kernel": "attend_mfma_kernel + attend_combine_kernel", "src": "attend.hip", "sha256": "053c38122d5216c8451cc9f17bdafa5255d98a3c1f42a277ee78d72159d98d1b", "fetch_kib": 75753.1, "write_kib": 17536.0, "fetch_scale": 1.9998, "write_scale": 1.0},
+    'hca_decode_1m': {"kernel": "attend_mfma_kernel + attend_combine_kernel", "src": "attend.hip", "sha256": "7ecf3628d32825a140dc0e8963b807f6116a1d2a6f0b1f10e08a7e180c5977b0", "fetch_kib": 75833.2, "write_kib": 17536.0, "fetch_scale": 1.9998, "write_scale": 1.0},
 }
 
 
